@@ -1,0 +1,409 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for attention with a per-row log2 LSE,
+ * split-KV partials and their merge.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or load
+ * this file: only the test suite, the package smoke check and the benchmark's CPU
+ * baseline do.  It shares no code, header, table or helper with the HIP library.
+ *
+ * Sources (page title, then section):
+ *   [P1] auto-round issue #2556, "ARK return_lse gives the same LSE for every 16
+ *        query rows (sdpa, sagev1, sageattn) on XPU": task statement, Problem
+ *        Description, Reproduction Steps (the reference LSE helper and the
+ *        smooth_k shift in part 3).
+ *   [P2] SGLang PR #33840, "[XPU] Support softmax_lse in sgl_kernel::fwd API":
+ *        review thread (varlen LSE is 2-D [num_heads, total_q]; total_q is the
+ *        row-major flattening of (batch, seq)).
+ *   [P3] ExecuTorch PR #22133, "Prevent Voxtral NaNs in CUDA split-K attention":
+ *        Copilot overview (per-split max tracking, global rescale in the reduce)
+ *        and the reviewer's item 3 (every partial slot is written).
+ *
+ * What is computed.  For query row i with key set J(i):
+ *     s_ij  = scale * sum_d q_id k_jd                      (fp64)
+ *     m_i   = max_j s_ij,  Z_i = sum_j exp(s_ij - m_i)
+ *     out_i = sum_j exp(s_ij - m_i) v_j / Z_i
+ *     lse_i = (m_i + ln Z_i) / ln 2
+ * i.e. P1's definition log2(sum_j exp(scale * q . k_j)) on unsmoothed logits,
+ * which its reproduction evaluates as a natural logsumexp divided by ln 2.
+ * The max is subtracted only so exp() stays in range; it cancels exactly.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   - empty key set (fully masked row, empty split): out = 0, lse = -inf;
+ *   - causal mask is bottom-right aligned: row i sees keys j <= i + Sk - Sq;
+ *   - GQA: q head h uses kv head h / (Hq / Hkv) (consecutive groups);
+ *   - split s covers keys [s*C, min((s+1)*C, Lkv)) with C = ceil(Lkv / S);
+ *   - mean(k) for smooth_k is taken over the call's keys per (batch, kv head),
+ *     per (sequence, kv head) for varlen.
+ *
+ * Inputs are raw 16-bit patterns (bf16 or fp16) decoded here by this file's own
+ * decoder, so the oracle sees exactly the values the GPU sees.
+ */
+#define _GNU_SOURCE
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_BF16 = 0, OR_FP16 = 1 };
+enum { OR_HND = 0, OR_NHD = 1 };
+
+/* ---------------------------------------------------------------- decoding */
+
+/* bf16 is the top half of an IEEE binary32: widen by shifting into place. */
+static double decode_bf16(uint16_t h) {
+    uint32_t w = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double decode_fp16(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -24);                 /* zero or subnormal */
+    else if (e == 31)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + f), e - 25);     /* (1 + f/1024) * 2^(e-15) */
+    return sign ? -mag : mag;
+}
+
+static double decode(uint16_t h, int dtype) {
+    return dtype == OR_BF16 ? decode_bf16(h) : decode_fp16(h);
+}
+
+/* Decode n patterns; exposed so the decoder itself can be checked. */
+void oracle_decode(const uint16_t* in, int64_t n, int dtype, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = decode(in[i], dtype);
+}
+
+/* ------------------------------------------------------------ addressing */
+
+/* Element offset of (b, h, s, 0) in a [B,H,S,D] (HND) or [B,S,H,D] (NHD) tensor. */
+static int64_t row_offset(int layout, int64_t b, int64_t h, int64_t s,
+                          int64_t H, int64_t S, int64_t D) {
+    if (layout == OR_HND) return ((b * H + h) * S + s) * D;
+    return ((b * S + s) * H + h) * D;
+}
+
+/* --------------------------------------------------------- one query row */
+
+/*
+ * Attention of one query row q (length D, already decoded) against the keys
+ * key_ptr(j) / value_ptr(j), j in [0, n).  Writes out[D] and returns lse (log2).
+ * kbar, when non-NULL, is subtracted from every key first (the smoothed logits).
+ * s is caller-provided scratch of n doubles.
+ */
+typedef struct {
+    const uint16_t* k;
+    const uint16_t* v;
+    int dtype;
+    int64_t stride;      /* elements between consecutive keys */
+} kv_view;
+
+static double attend_row(const double* q, int D, const kv_view* kv, int64_t n,
+                         double scale, const double* kbar, double* s, double* out) {
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    if (n <= 0) return -INFINITY;                    /* empty key set */
+
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+        const uint16_t* kj = kv->k + j * kv->stride;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) {
+            double kd = decode(kj[d], kv->dtype);
+            if (kbar) kd -= kbar[d];
+            dot += q[d] * kd;
+        }
+        s[j] = scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        double p = exp(s[j] - m);
+        z += p;
+        const uint16_t* vj = kv->v + j * kv->stride;
+        for (int d = 0; d < D; ++d) out[d] += p * decode(vj[d], kv->dtype);
+    }
+    for (int d = 0; d < D; ++d) out[d] /= z;
+    return (m + log(z)) / M_LN2;
+}
+
+/* Number of keys row i may see: all of them, or j <= i + Sk - Sq when causal. */
+static int64_t visible_keys(int64_t i, int64_t Sq, int64_t Sk, int causal) {
+    if (!causal) return Sk;
+    int64_t n = i + Sk - Sq + 1;
+    if (n < 0) n = 0;
+    if (n > Sk) n = Sk;
+    return n;
+}
+
+/* --------------------------------------------------------------- mean(k) */
+
+/*
+ * kbar[b, g, :] = mean over keys [j0, j1) of k[b, g, j, :] (fp64).  P1 part 3
+ * takes the mean of K along its key axis per (batch, head).
+ */
+static void kmean_range(const uint16_t* k, int dtype, int layout, int64_t b, int64_t g,
+                        int64_t Hkv, int64_t Sk, int D, int64_t j0, int64_t j1,
+                        double* kbar) {
+    for (int d = 0; d < D; ++d) kbar[d] = 0.0;
+    for (int64_t j = j0; j < j1; ++j) {
+        const uint16_t* kj = k + row_offset(layout, b, g, j, Hkv, Sk, D);
+        for (int d = 0; d < D; ++d) kbar[d] += decode(kj[d], dtype);
+    }
+    int64_t n = j1 - j0;
+    for (int d = 0; d < D; ++d) kbar[d] = n > 0 ? kbar[d] / (double)n : 0.0;
+}
+
+void oracle_kmean(const uint16_t* k, int dtype, int layout, int B, int Hkv, int Sk, int D,
+                  double* kbar /* [B, Hkv, D] */) {
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t g = 0; g < Hkv; ++g)
+            kmean_range(k, dtype, layout, b, g, Hkv, Sk, D, 0, Sk,
+                        kbar + (b * Hkv + g) * D);
+}
+
+/* --------------------------------------------------------- dense forward */
+
+/*
+ * Dense attention.  q is [B,Hq,Sq,D] (HND) or [B,Sq,Hq,D] (NHD); k, v likewise
+ * with Hkv and Sk.  out has q's layout; lse is [B, Hq, Sq] (P1 Problem
+ * Description: the LSE has shape [B, H, S_q]).
+ * smoothed != 0 computes the logits on k - mean(k) instead and returns that
+ * (smoothed) LSE without any add-back: it exists only to check the add-back
+ * identity of P1 part 3.  Returns 0, or -1 on bad arguments / no memory.
+ */
+int oracle_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype, int layout,
+                int B, int Hq, int Hkv, int Sq, int Sk, int D, double scale, int causal,
+                int smoothed, double* out, double* lse) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Sq < 0 || Sk < 0 || D <= 0) return -1;
+    const int G = Hq / Hkv;
+    double* kbar = NULL;
+    if (smoothed) {
+        kbar = (double*)malloc(sizeof(double) * (size_t)B * Hkv * D);
+        if (!kbar) return -1;
+        oracle_kmean(k, dtype, layout, B, Hkv, Sk, D, kbar);
+    }
+    const int64_t kstride = layout == OR_HND ? D : (int64_t)Hkv * D;
+    int err = 0;
+    #pragma omp parallel
+    {
+        double* qd = (double*)malloc(sizeof(double) * D);
+        double* s = (double*)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
+        if (!qd || !s) {
+            #pragma omp atomic write
+            err = 1;
+        } else {
+            #pragma omp for collapse(3) schedule(dynamic, 4)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t h = 0; h < Hq; ++h)
+                    for (int64_t i = 0; i < Sq; ++i) {
+                        const int64_t g = h / G;
+                        const uint16_t* qi = q + row_offset(layout, b, h, i, Hq, Sq, D);
+                        for (int d = 0; d < D; ++d) qd[d] = decode(qi[d], dtype);
+                        kv_view kv = {k + row_offset(layout, b, g, 0, Hkv, Sk, D),
+                                      v + row_offset(layout, b, g, 0, Hkv, Sk, D),
+                                      dtype, kstride};
+                        double r = attend_row(qd, D, &kv, visible_keys(i, Sq, Sk, causal),
+                                              scale, kbar ? kbar + (b * Hkv + g) * D : NULL,
+                                              s, out + row_offset(layout, b, h, i, Hq, Sq, D));
+                        lse[(b * Hq + h) * Sq + i] = r;
+                    }
+        }
+        free(qd);
+        free(s);
+    }
+    free(kbar);
+    return err ? -1 : 0;
+}
+
+/*
+ * The same quantities for a chosen list of rows only, so that full-size
+ * problems can be checked on a sample.  rows holds n triples (b, h, i).
+ * out is [n, D], lse is [n].
+ */
+int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
+                     int layout, int B, int Hq, int Hkv, int Sq, int Sk, int D, double scale,
+                     int causal, const int64_t* rows, int64_t n, double* out, double* lse) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Sq <= 0 || Sk < 0 || D <= 0) return -1;
+    const int G = Hq / Hkv;
+    const int64_t kstride = layout == OR_HND ? D : (int64_t)Hkv * D;
+    int err = 0;
+    #pragma omp parallel
+    {
+        double* qd = (double*)malloc(sizeof(double) * D);
+        double* s = (double*)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
+        if (!qd || !s) {
+            #pragma omp atomic write
+            err = 1;
+        } else {
+            #pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < n; ++r) {
+                const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+                if (b < 0 || b >= B || h < 0 || h >= Hq || i < 0 || i >= Sq) {
+                    #pragma omp atomic write
+                    err = 1;
+                    continue;
+                }
+                const int64_t g = h / G;
+                const uint16_t* qi = q + row_offset(layout, b, h, i, Hq, Sq, D);
+                for (int d = 0; d < D; ++d) qd[d] = decode(qi[d], dtype);
+                kv_view kv = {k + row_offset(layout, b, g, 0, Hkv, Sk, D),
+                              v + row_offset(layout, b, g, 0, Hkv, Sk, D), dtype, kstride};
+                lse[r] = attend_row(qd, D, &kv, visible_keys(i, Sq, Sk, causal), scale, NULL,
+                                    s, out + r * D);
+            }
+        }
+        free(qd);
+        free(s);
+    }
+    return err ? -1 : 0;
+}
+
+/* -------------------------------------------------------- varlen forward */
+
+/*
+ * Packed variable-length attention.  Sequence b owns query tokens
+ * [cu_q[b], cu_q[b+1]) and key tokens [cu_k[b], cu_k[b+1]).  q and out are
+ * [total_q, Hq, D], k and v are [total_k, Hkv, D].  lse is 2-D [Hq, total_q]
+ * (P2 review thread: the varlen kernel returns [num_heads, total_q]).
+ */
+int oracle_attn_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
+                       const int32_t* cu_q, const int32_t* cu_k, int nseq, int Hq, int Hkv,
+                       int D, double scale, int causal, double* out, double* lse) {
+    if (nseq < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0) return -1;
+    const int G = Hq / Hkv;
+    const int64_t total_q = cu_q[nseq];
+    int64_t max_k = 1;
+    for (int b = 0; b < nseq; ++b) {
+        if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return -1;
+        if (cu_k[b + 1] - cu_k[b] > max_k) max_k = cu_k[b + 1] - cu_k[b];
+    }
+    int err = 0;
+    #pragma omp parallel
+    {
+        double* qd = (double*)malloc(sizeof(double) * D);
+        double* s = (double*)malloc(sizeof(double) * max_k);
+        if (!qd || !s) {
+            #pragma omp atomic write
+            err = 1;
+        } else {
+            #pragma omp for collapse(2) schedule(dynamic, 16)
+            for (int64_t t = 0; t < total_q; ++t)
+                for (int64_t h = 0; h < Hq; ++h) {
+                    int b = 0;
+                    while (t >= cu_q[b + 1]) ++b;    /* sequence owning token t */
+                    const int64_t i = t - cu_q[b];
+                    const int64_t Lq = cu_q[b + 1] - cu_q[b];
+                    const int64_t Lk = cu_k[b + 1] - cu_k[b];
+                    const int64_t g = h / G;
+                    const uint16_t* qi = q + (t * Hq + h) * D;
+                    for (int d = 0; d < D; ++d) qd[d] = decode(qi[d], dtype);
+                    kv_view kv = {k + ((int64_t)cu_k[b] * Hkv + g) * D,
+                                  v + ((int64_t)cu_k[b] * Hkv + g) * D, dtype,
+                                  (int64_t)Hkv * D};
+                    lse[h * total_q + t] = attend_row(qd, D, &kv, visible_keys(i, Lq, Lk, causal),
+                                                      scale, NULL, s, out + (t * Hq + h) * D);
+                }
+        }
+        free(qd);
+        free(s);
+    }
+    return err ? -1 : 0;
+}
+
+/* ------------------------------------------------------- split partials */
+
+/*
+ * Split-KV partial states.  Chunk s covers keys [s*C, min((s+1)*C, Lkv)),
+ * C = ceil(Lkv / S).  For each chunk, every row gets the attention restricted
+ * to that chunk: o normalised by the chunk's own sum and its own log2 LSE.
+ * An empty chunk still gets a state, (0, -inf) (P3 reviewer item 3: every
+ * partial slot is written).  q is [B,Hq,Lq,D]/[B,Lq,Hq,D]; out_part is
+ * [S,B,Hq,Lq,D] and lse_part [S,B,Hq,Lq], both in HND row order.
+ */
+int oracle_splitkv_partials(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
+                            int layout, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                            double scale, int S, double* out_part, double* lse_part) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lq <= 0 || Lkv < 0 || D <= 0 || S <= 0)
+        return -1;
+    const int G = Hq / Hkv;
+    const int64_t C = ((int64_t)Lkv + S - 1) / S;
+    const int64_t kstride = layout == OR_HND ? D : (int64_t)Hkv * D;
+    const int64_t rows = (int64_t)B * Hq * Lq;
+    int err = 0;
+    #pragma omp parallel
+    {
+        double* qd = (double*)malloc(sizeof(double) * D);
+        double* s = (double*)malloc(sizeof(double) * (C > 0 ? C : 1));
+        if (!qd || !s) {
+            #pragma omp atomic write
+            err = 1;
+        } else {
+            #pragma omp for collapse(4) schedule(dynamic, 4)
+            for (int64_t sp = 0; sp < S; ++sp)
+                for (int64_t b = 0; b < B; ++b)
+                    for (int64_t h = 0; h < Hq; ++h)
+                        for (int64_t i = 0; i < Lq; ++i) {
+                            const int64_t g = h / G;
+                            int64_t j0 = sp * C, j1 = (sp + 1) * C;
+                            if (j0 > Lkv) j0 = Lkv;
+                            if (j1 > Lkv) j1 = Lkv;
+                            const uint16_t* qi = q + row_offset(layout, b, h, i, Hq, Lq, D);
+                            for (int d = 0; d < D; ++d) qd[d] = decode(qi[d], dtype);
+                            kv_view kv = {k + row_offset(layout, b, g, j0, Hkv, Lkv, D),
+                                          v + row_offset(layout, b, g, j0, Hkv, Lkv, D),
+                                          dtype, kstride};
+                            const int64_t r = (b * Hq + h) * Lq + i;
+                            lse_part[sp * rows + r] =
+                                attend_row(qd, D, &kv, j1 - j0, scale, NULL, s,
+                                           out_part + (sp * rows + r) * D);
+                        }
+        }
+        free(qd);
+        free(s);
+    }
+    return err ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ merge */
+
+/*
+ * Merge S partial states (o_s, lse_s) of R rows into one, the stable way of
+ * P3's Copilot overview: take the global max M of the partial LSEs, weight
+ * each partial by w_s = 2^(lse_s - M), and normalise by the sum of weights:
+ *     out = sum_s w_s o_s / sum_s w_s,   lse = M + log2 sum_s w_s.
+ * A partial with lse = -inf has weight 0; if every partial is -inf the row is
+ * empty and gets (0, -inf).  o_parts is [S, R, D], lse_parts [S, R].
+ */
+void oracle_merge(int S, int64_t R, int D, const double* o_parts, const double* lse_parts,
+                  double* out, double* lse) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        double M = -INFINITY;
+        for (int s = 0; s < S; ++s)
+            if (lse_parts[s * R + r] > M) M = lse_parts[s * R + r];
+        double* o = out + r * D;
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (M == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double wsum = 0.0;
+        for (int s = 0; s < S; ++s) {
+            double l = lse_parts[s * R + r];
+            if (l == -INFINITY) continue;
+            double w = exp2(l - M);
+            wsum += w;
+            const double* os = o_parts + (s * R + r) * D;
+            for (int d = 0; d < D; ++d) o[d] += w * os[d];
+        }
+        for (int d = 0; d < D; ++d) o[d] /= wsum;
+        lse[r] = M + log2(wsum);
+    }
+}
