@@ -1,0 +1,186 @@
+/*
+ * skv.h -- C ABI of the split-KV attention library for MI355X (gfx950).
+ *
+ * Attention forward that returns its output plus one log-sum-exp per query row,
+ * the split-KV decode step that produces per-chunk partial (out, LSE) states, and
+ * the stable merge of such states.
+ *
+ * Sources (page title, then section):
+ *   [ARK]  auto-round issue #2556, "ARK return_lse gives the same LSE for every 16
+ *          query rows (sdpa, sagev1, sageattn) on XPU" -- task statement, Problem
+ *          Description, Reproduction Steps.
+ *   [SGL]  SGLang PR #33840, "[XPU] Support softmax_lse in sgl_kernel::fwd API" --
+ *          Modifications, review thread.
+ *   [ET]   ExecuTorch PR #22133, "Prevent Voxtral NaNs in CUDA split-K attention" --
+ *          description, Copilot overview, reviewer comments 1-3.
+ *   [ASC]  SGLang error record "Unexpected Ascend TND softmax LSE shape".
+ *
+ * Conventions shared by every call
+ *   - LSE means log2( sum_j exp(scale * q_i . k_j) ) over the keys row i sees, on the
+ *     original unsmoothed logits, one value per query row [ARK task statement and
+ *     Problem Description].  It is float32.  A row that sees no key gets LSE = -inf
+ *     and an all-zero output row.
+ *   - Outputs are written in place into caller memory; a call returns only a status
+ *     and an optional LSE pointer may be NULL, meaning "not wanted" [SGL
+ *     Modifications; review thread on has_value()].
+ *   - All tensor pointers are DEVICE pointers (k and v may be NULL when there is no
+ *     key to read), contiguous in the named layout, with
+ *     the head dimension D innermost; q/k/v/out must be 16-byte aligned, LSE
+ *     buffers 4-byte aligned.  The caller owns every buffer; the library keeps no
+ *     state, allocates nothing and never synchronises: each call only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL = the default stream), so calls can
+ *     be captured into a HIP graph.
+ *   - Shapes are checked before anything is launched or written [SGL review:
+ *     check before reshaping; ASC record: shape guard]; a rejected call returns
+ *     SKV_EINVAL (malformed) or SKV_EUNSUPPORTED (valid but not built, e.g.
+ *     D = 96) and touches no memory.  A launch failure returns SKV_ELAUNCH.
+ *     skv_last_error() then describes the reason.  No C++ exception crosses the ABI.
+ *   - GQA: Hq must be a multiple of Hkv; q head h reads kv head h / (Hq / Hkv).
+ *   - Supported: D in {64, 128, 256}; q/k/v in bf16 or fp16.
+ *   - Layouts: SKV_HND = [B, H, S, D], SKV_NHD = [B, S, H, D] [ARK Problem
+ *     Description: both tensor_layout values].
+ */
+#ifndef SKV_H_
+#define SKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SKV_OK = 0,
+    SKV_EINVAL = 1,        /* malformed arguments: nothing launched, nothing written */
+    SKV_EUNSUPPORTED = 2,  /* well-formed but outside what is built (D, dtype, rows) */
+    SKV_ELAUNCH = 3        /* the HIP runtime refused a launch */
+} skv_status_t;
+
+typedef enum { SKV_BF16 = 0, SKV_FP16 = 1, SKV_FP32 = 2 } skv_dtype_t;
+typedef enum { SKV_HND = 0, SKV_NHD = 1 } skv_layout_t;
+
+/*
+ * Dense attention forward with an optional per-row LSE.
+ *
+ *   q   [B, Hq, Sq, D] (HND) or [B, Sq, Hq, D] (NHD), dtype
+ *   k,v [B, Hkv, Sk, D] or [B, Sk, Hkv, D], dtype
+ *   out same shape and layout as q, dtype (round to nearest even)
+ *   lse float32 [B, Hq, Sq] or NULL
+ *
+ * out_i = sum_j softmax_j(scale * q_i . k_j) v_j.  causal != 0 masks keys with
+ * j > i + Sk - Sq (bottom-right aligned; j <= i when Sq == Sk).
+ *
+ * smooth_k != 0 computes the logits against k - mean(k), the mean taken over this
+ * call's Sk keys per (batch, kv head), and adds scale * q_i . mean(k) back into
+ * the LSE, so the LSE still refers to the unsmoothed logits [ARK Problem
+ * Description, second issue; Reproduction Steps part 3].  The output is
+ * unchanged by smoothing.  It needs a float32 workspace of
+ * skv_workspace_bytes(B, Hkv, D, 1) bytes (device memory, 16-byte aligned, no
+ * initialisation required); without smoothing `workspace` may be NULL.
+ *
+ * Sizes: B, Sq, Sk >= 0 (zero-sized problems return SKV_OK without launching,
+ * except Sk == 0 with Sq > 0, which writes zero outputs and -inf LSEs).
+ */
+skv_status_t skv_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int Sq, int Sk, int D, skv_dtype_t dtype,
+                          skv_layout_t layout, float scale, int causal, int smooth_k,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Packed variable-length attention forward [SGL review thread; ASC record].
+ *
+ *   q, out [total_q, Hq, D] and k, v [total_k, Hkv, D], dtype, token-major packed.
+ *   cu_seqlens_q, cu_seqlens_k: DEVICE int32 [nseq + 1], non-decreasing, starting
+ *     at 0 and ending at total_q / total_k; sequence b owns query tokens
+ *     [cu_q[b], cu_q[b+1]) and key tokens [cu_k[b], cu_k[b+1]).  Their contents are
+ *     not validated on the host (that would need a synchronisation); malformed
+ *     values are undefined behaviour.
+ *   max_seqlen_q: an upper bound on every query length (sizes the grid).
+ *   lse: float32 [Hq, total_q] (2-D: head-major, token index as in q) or NULL.
+ *
+ * causal and smooth_k act per sequence as in skv_attn_fwd (mean(k) per sequence
+ * and kv head; workspace of skv_workspace_bytes(nseq, Hkv, D, 1) bytes).
+ */
+skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
+                                 float* lse, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                 int total_k, int max_seqlen_q, int Hq, int Hkv, int D,
+                                 skv_dtype_t dtype, float scale, int causal, int smooth_k,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Split-KV decode step: per-chunk partial attention states [ET description and
+ * Copilot overview: per-split online softmax with its own running max].
+ *
+ *   q   [B, Hq, Lq, D] (HND) or [B, Lq, Hq, D] (NHD), dtype; every query row sees
+ *       every key (no causal mask).
+ *   k,v [B, Hkv, Lkv, D] or [B, Lkv, Hkv, D], dtype
+ *   out_part float32 [num_splits, <q's shape>]: chunk s's output normalised by its
+ *       own softmax sum.
+ *   lse_part float32 [num_splits, B, Hq, Lq]: chunk s's LSE (log2).
+ *
+ * Chunk s covers keys [s*C, min((s+1)*C, Lkv)) with C = ceil(Lkv / num_splits).
+ * Every slot of both buffers is written, including chunks that hold no key, which
+ * get (0, -inf) [ET reviewer item 3: no early exit for empty splits], so neither
+ * buffer needs initialising.  Merge the states with skv_merge_state.
+ * Limits: Lq >= 1, Lkv >= 0, num_splits >= 1, (Hq / Hkv) * Lq <= 16
+ * (SKV_EUNSUPPORTED beyond).
+ */
+skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* v,
+                                      float* out_part, float* lse_part, int B, int Hq,
+                                      int Hkv, int Lq, int Lkv, int D, skv_dtype_t dtype,
+                                      skv_layout_t layout, float scale, int num_splits,
+                                      void* stream);
+
+/*
+ * Stable merge of num_parts partial states (o_s, lse_s) per row [ET Copilot
+ * overview: global max over splits, rescale each split, reduce all together;
+ * reviewer item 2: keep the exponentials off a serial chain, parallelise over D].
+ *
+ * For each row:  M = max_s lse_s;  w_s = 2^(lse_s - M);
+ *                out = sum_s w_s o_s / sum_s w_s;  lse = M + log2(sum_s w_s).
+ * Parts with lse_s = -inf get weight 0; if all are -inf the row gets out = 0 and
+ * lse = -inf.
+ *
+ * Rows are addressed by a 3-D index (r0, r1, r2) in [R0) x [R1) x [R2); strides are
+ * in ELEMENTS of the pointed-to type, D is contiguous.  Element d of part s of row
+ * (r0, r1, r2) is parts_out[s * part_stride + r0 * strides[0] + r1 * strides[1] +
+ * r2 * strides[2] + d]; likewise for parts_lse, out and lse.  One call thus serves
+ * HND, NHD and the varlen [Hq, total_q] LSE.
+ *
+ *   parts_out  dtype parts_dtype (SKV_FP32, SKV_BF16 or SKV_FP16)
+ *   parts_lse  float32
+ *   out        dtype out_dtype (SKV_FP32, SKV_BF16 or SKV_FP16)
+ *   lse        float32, or NULL
+ * Vector access requires parts_out / out 16-byte aligned and their row strides and
+ * part stride multiples of 16 bytes.  num_parts >= 1; D in {64, 128, 256}.
+ */
+skv_status_t skv_merge_state(int num_parts, int R0, int R1, int R2, int D,
+                             const void* parts_out, skv_dtype_t parts_dtype,
+                             int64_t parts_out_part_stride, const int64_t parts_out_strides[3],
+                             const float* parts_lse, int64_t parts_lse_part_stride,
+                             const int64_t parts_lse_strides[3],
+                             void* out, skv_dtype_t out_dtype, const int64_t out_strides[3],
+                             float* lse, const int64_t lse_strides[3], void* stream);
+
+/* Workspace bytes skv_attn_fwd / skv_attn_fwd_varlen need: the float32 mean(k)
+ * buffer [B_or_nseq, Hkv, D] when smooth_k != 0, else 0. */
+size_t skv_workspace_bytes(int B_or_nseq, int Hkv, int D, int smooth_k);
+
+/* A split count for skv_attn_splitkv_partial: enough (batch, kv head, chunk) work
+ * groups to cover the 256 compute units several times, with chunks of at least a
+ * few 32-key blocks.  Pure host arithmetic; returns >= 1. */
+int skv_pick_num_splits(int B, int Hkv, int rows_per_kv_head, int Lkv, int D);
+
+/* Static description of a status code. */
+const char* skv_status_str(skv_status_t status);
+
+/* Description of the last error returned on the calling thread ("" if none). */
+const char* skv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKV_H_ */

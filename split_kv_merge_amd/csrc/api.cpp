@@ -1,0 +1,310 @@
+// api.cpp -- the C ABI of include/skv.h: argument validation, stride set-up and
+// kernel dispatch.  Every check runs before the first launch, so a rejected call
+// neither launches nor writes (SGLang PR #33840 review: check before reshaping;
+// SGLang's "Unexpected Ascend TND softmax LSE shape" record: guard shapes).
+#include "skv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+skv_status_t fail(skv_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+void clear_err() { g_err[0] = '\0'; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool is16(int dt) { return dt == SKV_BF16 || dt == SKV_FP16; }
+bool valid_dtype(int dt) { return dt == SKV_BF16 || dt == SKV_FP16 || dt == SKV_FP32; }
+int dtype_bytes(int dt) { return dt == SKV_FP32 ? 4 : 2; }
+bool valid_layout(int l) { return l == SKV_HND || l == SKV_NHD; }
+bool supported_D(int D) { return D == 64 || D == 128 || D == 256; }
+
+// product of non-negative factors without int64 overflow
+bool mul_ok(int64_t& acc, int64_t f) {
+    if (f < 0) return false;
+    if (f != 0 && acc > INT64_MAX / f) return false;
+    acc *= f;
+    return true;
+}
+bool elems_ok(std::initializer_list<int64_t> dims) {
+    int64_t acc = 1;
+    for (int64_t d : dims)
+        if (!mul_ok(acc, d)) return false;
+    return true;
+}
+
+skv_status_t launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SKV_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+    return SKV_OK;
+}
+
+// Checks shared by the attention entry points.  Returns SKV_OK or the error.
+skv_status_t check_heads_dims(int Hq, int Hkv, int D, int dtype) {
+    if (Hq <= 0 || Hkv <= 0) return fail(SKV_EINVAL, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
+    if (Hq % Hkv != 0)
+        return fail(SKV_EINVAL, "Hq (%d) must be a multiple of Hkv (%d) for grouped-query attention", Hq, Hkv);
+    if (Hq > 65535) return fail(SKV_EUNSUPPORTED, "Hq=%d exceeds the 65535 grid limit", Hq);
+    if (D <= 0) return fail(SKV_EINVAL, "head dimension D must be positive (D=%d)", D);
+    if (!supported_D(D)) return fail(SKV_EUNSUPPORTED, "head dimension D=%d is not built (64, 128, 256)", D);
+    if (!valid_dtype(dtype)) return fail(SKV_EINVAL, "unknown dtype code %d", dtype);
+    if (!is16(dtype)) return fail(SKV_EUNSUPPORTED, "q/k/v must be bf16 or fp16");
+    return SKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* skv_status_str(skv_status_t status) {
+    switch (status) {
+        case SKV_OK: return "ok";
+        case SKV_EINVAL: return "invalid argument";
+        case SKV_EUNSUPPORTED: return "unsupported configuration";
+        case SKV_ELAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char* skv_last_error(void) { return g_err; }
+
+size_t skv_workspace_bytes(int B_or_nseq, int Hkv, int D, int smooth_k) {
+    if (!smooth_k || B_or_nseq <= 0 || Hkv <= 0 || D <= 0) return 0;
+    return (size_t)B_or_nseq * (size_t)Hkv * (size_t)D * sizeof(float);
+}
+
+int skv_pick_num_splits(int B, int Hkv, int rows_per_kv_head, int Lkv, int D) {
+    (void)rows_per_kv_head;
+    (void)D;
+    if (B <= 0 || Hkv <= 0 || Lkv <= 0) return 1;
+    // Aim for ~4 work groups per compute unit (256 CUs) while keeping at least
+    // 128 keys (one 32-key block per wave) in every chunk.
+    const int64_t units = (int64_t)B * Hkv;
+    const int64_t target = 1024;
+    int64_t s = (target + units - 1) / units;
+    int64_t smax = Lkv / 128;
+    if (smax < 1) smax = 1;
+    if (s > smax) s = smax;
+    if (s > 256) s = 256;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+skv_status_t skv_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int Sq, int Sk, int D, skv_dtype_t dtype,
+                          skv_layout_t layout, float scale, int causal, int smooth_k,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    clear_err();
+    if (!q || !out) return fail(SKV_EINVAL, "q and out must be non-NULL");
+    if ((!k || !v) && Sk > 0) return fail(SKV_EINVAL, "k and v must be non-NULL when Sk > 0");
+    if (B < 0 || Sq < 0 || Sk < 0)
+        return fail(SKV_EINVAL, "sizes must be non-negative (B=%d, Sq=%d, Sk=%d)", B, Sq, Sk);
+    skv_status_t st = check_heads_dims(Hq, Hkv, D, dtype);
+    if (st != SKV_OK) return st;
+    if (!valid_layout(layout)) return fail(SKV_EINVAL, "unknown layout code %d", (int)layout);
+    if (!std::isfinite(scale)) return fail(SKV_EINVAL, "scale must be finite");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(SKV_EINVAL, "q, k, v and out must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(SKV_EINVAL, "lse must be 4-byte aligned");
+    if (B > 65535) return fail(SKV_EUNSUPPORTED, "B=%d exceeds the 65535 grid limit", B);
+    if (!elems_ok({B, Hq, Sq, D}) || !elems_ok({B, Hkv, Sk, D}))
+        return fail(SKV_EINVAL, "tensor sizes overflow 64-bit indexing");
+    const size_t need = skv_workspace_bytes(B, Hkv, D, smooth_k);
+    if (smooth_k && B > 0) {
+        if (!workspace || !aligned(workspace, 16))
+            return fail(SKV_EINVAL, "smooth_k needs a 16-byte aligned workspace");
+        if (workspace_bytes < need)
+            return fail(SKV_EINVAL, "workspace has %zu bytes, smooth_k needs %zu", workspace_bytes, need);
+    }
+    if (B == 0 || Sq == 0) return SKV_OK;
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool hnd = layout == SKV_HND;
+    skv::FmhaArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk;
+    a.q_row = hnd ? D : (int64_t)Hq * D;
+    a.q_head = hnd ? (int64_t)Sq * D : D;
+    a.q_batch = (int64_t)Hq * Sq * D;
+    a.kv_row = hnd ? D : (int64_t)Hkv * D;
+    a.kv_head = hnd ? (int64_t)Sk * D : D;
+    a.kv_batch = (int64_t)Hkv * Sk * D;
+    a.lse_head = Sq;
+    a.lse_batch = (int64_t)Hq * Sq;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    if (smooth_k) {
+        skv::KmeanArgs km{};
+        km.k = k; km.kbar = (float*)workspace; km.Hkv = Hkv; km.Sk = Sk;
+        km.kv_row = a.kv_row; km.kv_head = a.kv_head; km.kv_batch = a.kv_batch;
+        st = launched(skv::launch_kmean(km, dtype, D, false, B, s), "kmean");
+        if (st != SKV_OK) return st;
+        a.kbar = (const float*)workspace;
+    }
+    const int bm = skv::fmha_rows_per_block();
+    const int grid_m = (int)(((int64_t)Sq + bm - 1) / bm);
+    return launched(skv::launch_fmha(a, dtype, D, causal != 0, false, grid_m, B, s), "fmha_fwd");
+}
+
+skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
+                                 float* lse, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                 int total_k, int max_seqlen_q, int Hq, int Hkv, int D,
+                                 skv_dtype_t dtype, float scale, int causal, int smooth_k,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    clear_err();
+    if (!q || !out) return fail(SKV_EINVAL, "q and out must be non-NULL");
+    if ((!k || !v) && total_k > 0) return fail(SKV_EINVAL, "k and v must be non-NULL when total_k > 0");
+    if (nseq < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0)
+        return fail(SKV_EINVAL, "sizes must be non-negative (nseq=%d, total_q=%d, total_k=%d, max_seqlen_q=%d)",
+                    nseq, total_q, total_k, max_seqlen_q);
+    if (nseq > 0 && (!cu_seqlens_q || !cu_seqlens_k))
+        return fail(SKV_EINVAL, "cu_seqlens_q and cu_seqlens_k must be non-NULL");
+    if (max_seqlen_q > total_q)
+        return fail(SKV_EINVAL, "max_seqlen_q (%d) exceeds total_q (%d)", max_seqlen_q, total_q);
+    skv_status_t st = check_heads_dims(Hq, Hkv, D, dtype);
+    if (st != SKV_OK) return st;
+    if (!std::isfinite(scale)) return fail(SKV_EINVAL, "scale must be finite");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(SKV_EINVAL, "q, k, v and out must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(SKV_EINVAL, "lse must be 4-byte aligned");
+    if ((cu_seqlens_q && !aligned(cu_seqlens_q, 4)) || (cu_seqlens_k && !aligned(cu_seqlens_k, 4)))
+        return fail(SKV_EINVAL, "cu_seqlens must be 4-byte aligned");
+    if (nseq > 65535) return fail(SKV_EUNSUPPORTED, "nseq=%d exceeds the 65535 grid limit", nseq);
+    if (!elems_ok({total_q, Hq, D}) || !elems_ok({total_k, Hkv, D}))
+        return fail(SKV_EINVAL, "tensor sizes overflow 64-bit indexing");
+    const size_t need = skv_workspace_bytes(nseq, Hkv, D, smooth_k);
+    if (smooth_k && nseq > 0) {
+        if (!workspace || !aligned(workspace, 16))
+            return fail(SKV_EINVAL, "smooth_k needs a 16-byte aligned workspace");
+        if (workspace_bytes < need)
+            return fail(SKV_EINVAL, "workspace has %zu bytes, smooth_k needs %zu", workspace_bytes, need);
+    }
+    if (nseq == 0 || total_q == 0 || max_seqlen_q == 0) return SKV_OK;
+
+    hipStream_t s = (hipStream_t)stream;
+    skv::FmhaArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.Hq = Hq; a.Hkv = Hkv;
+    a.q_row = (int64_t)Hq * D; a.q_head = D; a.q_batch = 0;
+    a.kv_row = (int64_t)Hkv * D; a.kv_head = D; a.kv_batch = 0;
+    a.lse_head = total_q; a.lse_batch = 0;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    if (smooth_k) {
+        skv::KmeanArgs km{};
+        km.k = k; km.kbar = (float*)workspace; km.cu_k = cu_seqlens_k; km.Hkv = Hkv;
+        km.kv_row = a.kv_row; km.kv_head = a.kv_head;
+        st = launched(skv::launch_kmean(km, dtype, D, true, nseq, s), "kmean");
+        if (st != SKV_OK) return st;
+        a.kbar = (const float*)workspace;
+    }
+    const int bm = skv::fmha_rows_per_block();
+    const int grid_m = (max_seqlen_q + bm - 1) / bm;
+    return launched(skv::launch_fmha(a, dtype, D, causal != 0, true, grid_m, nseq, s), "fmha_fwd_varlen");
+}
+
+skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* v,
+                                      float* out_part, float* lse_part, int B, int Hq,
+                                      int Hkv, int Lq, int Lkv, int D, skv_dtype_t dtype,
+                                      skv_layout_t layout, float scale, int num_splits,
+                                      void* stream) {
+    clear_err();
+    if (!q || !out_part || !lse_part)
+        return fail(SKV_EINVAL, "q, out_part and lse_part must be non-NULL");
+    if ((!k || !v) && Lkv > 0) return fail(SKV_EINVAL, "k and v must be non-NULL when Lkv > 0");
+    if (B < 0 || Lq < 1 || Lkv < 0)
+        return fail(SKV_EINVAL, "need B >= 0, Lq >= 1, Lkv >= 0 (B=%d, Lq=%d, Lkv=%d)", B, Lq, Lkv);
+    if (num_splits < 1) return fail(SKV_EINVAL, "num_splits must be >= 1 (got %d)", num_splits);
+    skv_status_t st = check_heads_dims(Hq, Hkv, D, dtype);
+    if (st != SKV_OK) return st;
+    if (!valid_layout(layout)) return fail(SKV_EINVAL, "unknown layout code %d", (int)layout);
+    if (!std::isfinite(scale)) return fail(SKV_EINVAL, "scale must be finite");
+    if ((int64_t)(Hq / Hkv) * Lq > 16)
+        return fail(SKV_EUNSUPPORTED, "(Hq/Hkv)*Lq = %lld query rows per kv head exceeds 16",
+                    (long long)(Hq / Hkv) * Lq);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out_part, 16))
+        return fail(SKV_EINVAL, "q, k, v and out_part must be 16-byte aligned");
+    if (!aligned(lse_part, 4)) return fail(SKV_EINVAL, "lse_part must be 4-byte aligned");
+    if (B > 65535 || Hkv > 65535) return fail(SKV_EUNSUPPORTED, "B or Hkv exceeds the 65535 grid limit");
+    if (!elems_ok({num_splits, B, Hq, Lq, D}) || !elems_ok({B, Hkv, Lkv, D}))
+        return fail(SKV_EINVAL, "tensor sizes overflow 64-bit indexing");
+    if (B == 0) return SKV_OK;
+
+    const bool hnd = layout == SKV_HND;
+    skv::SplitArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out_part = out_part; a.lse_part = lse_part;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lkv = Lkv; a.num_splits = num_splits;
+    a.q_row = hnd ? D : (int64_t)Hq * D;
+    a.q_head = hnd ? (int64_t)Lq * D : D;
+    a.q_batch = (int64_t)Hq * Lq * D;
+    a.kv_row = hnd ? D : (int64_t)Hkv * D;
+    a.kv_head = hnd ? (int64_t)Lkv * D : D;
+    a.kv_batch = (int64_t)Hkv * Lkv * D;
+    a.part_stride = (int64_t)B * Hq * Lq * D;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return launched(skv::launch_splitkv(a, dtype, D, (hipStream_t)stream), "splitkv_partial");
+}
+
+skv_status_t skv_merge_state(int num_parts, int R0, int R1, int R2, int D,
+                             const void* parts_out, skv_dtype_t parts_dtype,
+                             int64_t parts_out_part_stride, const int64_t parts_out_strides[3],
+                             const float* parts_lse, int64_t parts_lse_part_stride,
+                             const int64_t parts_lse_strides[3],
+                             void* out, skv_dtype_t out_dtype, const int64_t out_strides[3],
+                             float* lse, const int64_t lse_strides[3], void* stream) {
+    clear_err();
+    if (!parts_out || !parts_lse || !out)
+        return fail(SKV_EINVAL, "parts_out, parts_lse and out must be non-NULL");
+    if (!parts_out_strides || !parts_lse_strides || !out_strides || (lse && !lse_strides))
+        return fail(SKV_EINVAL, "stride arrays must be non-NULL");
+    if (num_parts < 1) return fail(SKV_EINVAL, "num_parts must be >= 1 (got %d)", num_parts);
+    if (R0 < 0 || R1 < 0 || R2 < 0) return fail(SKV_EINVAL, "row extents must be non-negative");
+    if (D <= 0) return fail(SKV_EINVAL, "D must be positive (D=%d)", D);
+    if (!supported_D(D)) return fail(SKV_EUNSUPPORTED, "D=%d is not built (64, 128, 256)", D);
+    if (!valid_dtype(parts_dtype) || !valid_dtype(out_dtype))
+        return fail(SKV_EINVAL, "unknown dtype code (parts %d, out %d)", (int)parts_dtype, (int)out_dtype);
+    const int pb = dtype_bytes(parts_dtype), ob = dtype_bytes(out_dtype);
+    if (!aligned(parts_out, 16) || !aligned(out, 16))
+        return fail(SKV_EINVAL, "parts_out and out must be 16-byte aligned");
+    if (!aligned(parts_lse, 4) || (lse && !aligned(lse, 4)))
+        return fail(SKV_EINVAL, "LSE buffers must be 4-byte aligned");
+    if ((parts_out_part_stride * pb) % 16 != 0)
+        return fail(SKV_EINVAL, "parts_out part stride must be a multiple of 16 bytes");
+    for (int i = 0; i < 3; ++i) {
+        if ((parts_out_strides[i] * pb) % 16 != 0 || (out_strides[i] * ob) % 16 != 0)
+            return fail(SKV_EINVAL, "row strides of parts_out and out must be multiples of 16 bytes");
+    }
+    int64_t rows = 1;
+    if (!mul_ok(rows, R0) || !mul_ok(rows, R1) || !mul_ok(rows, R2))
+        return fail(SKV_EINVAL, "row count overflows");
+    if (rows == 0) return SKV_OK;
+    if (rows > (int64_t)1 << 40) return fail(SKV_EUNSUPPORTED, "too many rows (%lld)", (long long)rows);
+
+    skv::MergeArgs a{};
+    a.parts_out = parts_out; a.parts_lse = parts_lse; a.out = out; a.lse = lse;
+    a.num_parts = num_parts; a.R1 = R1; a.R2 = R2; a.rows = rows;
+    a.po_part = parts_out_part_stride;
+    a.po_s0 = parts_out_strides[0]; a.po_s1 = parts_out_strides[1]; a.po_s2 = parts_out_strides[2];
+    a.pl_part = parts_lse_part_stride;
+    a.pl_s0 = parts_lse_strides[0]; a.pl_s1 = parts_lse_strides[1]; a.pl_s2 = parts_lse_strides[2];
+    a.o_s0 = out_strides[0]; a.o_s1 = out_strides[1]; a.o_s2 = out_strides[2];
+    if (lse) { a.l_s0 = lse_strides[0]; a.l_s1 = lse_strides[1]; a.l_s2 = lse_strides[2]; }
+    return launched(skv::launch_merge(a, parts_dtype, out_dtype, D, (hipStream_t)stream), "merge_state");
+}
+
+}  // extern "C"

@@ -1,0 +1,291 @@
+// fmha_fwd.hip -- fused attention forward with one log2 LSE per query row.
+//
+// Computes, per query row i, out_i = softmax_j(scale q_i . k_j) V and
+// LSE_i = log2 sum_j exp(scale q_i . k_j) on the unsmoothed logits (auto-round
+// #2556 "ARK return_lse gives the same LSE for every 16 query rows", task
+// statement and Problem Description).  Optional smoothing subtracts
+// scale * q_i . mean(k) from every logit of row i and adds it back in the LSE
+// (same report, second issue; Reproduction Steps part 3).
+//
+// Design (gfx950, wave64):
+//   * work group = 4 waves = 128 query rows; wave w owns rows [32w, 32w + 32).
+//   * S^T = K Q^T on v_mfma_f32_32x32x16 with keys on the M axis and query rows on
+//     the N (lane) axis, so every lane owns exactly one query row: its running
+//     max and sum live in that lane (plus its partner lane^32), and the LSE
+//     epilogue stores one value per row from one lane -- the per-row ownership the
+//     report's 16-row-block bug lacked.
+//   * Q stays in registers as the B operand for the whole key loop.  K and V tiles
+//     are staged global -> registers -> LDS (the next tile's loads are in flight
+//     while the current one is computed).
+//   * The C layout of S^T is reused directly as the B operand of O^T += V^T P^T;
+//     the key order inside P is permuted and V^T is read from LDS with
+//     ds_read_b64_tr_b16 in the matching permuted order (a sum over keys does not
+//     care about their order).
+//   * Online softmax in base 2: logits are scaled by scale*log2(e) with one
+//     multiply, p = exp2(s - m) (v_exp_f32), all statistics in fp32 registers.
+#include "device.h"
+#include "launch.h"
+
+namespace skv {
+
+namespace {
+
+template <int D> struct FmhaTile {
+    static constexpr int BM = 128;                 // query rows per work group
+    static constexpr int BN = D == 256 ? 32 : 64;  // keys per tile
+    static constexpr int KLD = D + 8;              // K row pitch in LDS (elements)
+    static constexpr int VLD = D + 16;             // V row pitch in LDS (elements)
+    static constexpr int NCH = BN * D / 8 / 256;   // 16-byte chunks per thread per tile
+};
+
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256) void fmha_fwd_kernel(FmhaArgs a) {
+    using E = Elem<T>;
+    typedef typename E::vec8 V8;
+    typedef FmhaTile<D> Tl;
+    constexpr int BM = Tl::BM, BN = Tl::BN, KLD = Tl::KLD, VLD = Tl::VLD, NCH = Tl::NCH;
+    constexpr int NKK = D / 16;   // MFMA k-steps over the head dimension
+    constexpr int NJB = BN / 32;  // 32-key blocks per tile
+    constexpr int NDB = D / 32;   // 32-wide blocks of the output head dimension
+    constexpr int CPR = D / 8;    // 16-byte chunks per K/V row
+
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * KLD];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[BN * VLD];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, hg = lane >> 5;
+    const int b = blockIdx.z, h = blockIdx.y;
+    // causal: the longest (last) row tiles first, so they do not trail the grid
+    const int mt = CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+
+    int Lq, Lk;
+    int64_t q_off, kv_off, lse_off;
+    if (VARLEN) {
+        const int q0 = a.cu_q[b], k0 = a.cu_k[b];
+        Lq = a.cu_q[b + 1] - q0;
+        Lk = a.cu_k[b + 1] - k0;
+        q_off = (int64_t)q0 * a.q_row;
+        kv_off = (int64_t)k0 * a.kv_row;
+        lse_off = q0;
+    } else {
+        Lq = a.Sq;
+        Lk = a.Sk;
+        q_off = (int64_t)b * a.q_batch;
+        kv_off = (int64_t)b * a.kv_batch;
+        lse_off = (int64_t)b * a.lse_batch;
+    }
+    const int m0 = mt * BM;
+    if (m0 >= Lq) return;  // uniform across the work group
+
+    const int g = h / (a.Hq / a.Hkv);
+    const uint16_t* qp = (const uint16_t*)a.q + q_off + (int64_t)h * a.q_head;
+    const uint16_t* kp = (const uint16_t*)a.k + kv_off + (int64_t)g * a.kv_head;
+    const uint16_t* vp = (const uint16_t*)a.v + kv_off + (int64_t)g * a.kv_head;
+
+    const int row = m0 + wave * 32 + n;
+    const bool row_ok = row < Lq;
+
+    // Q as the B operand: this lane holds q[row][hg*D/2 + 8kk .. +8) for each k-step.
+    V8 qf[NKK];
+    {
+        const uint16_t* qr = qp + (int64_t)row * a.q_row + hg * (D / 2);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (row_ok) raw = load16(qr + kk * 8);
+            qf[kk] = as_vec8<T>(raw);
+        }
+    }
+
+    // Smoothing bias in log2 units: scale*log2(e) * (q_row . mean(k)).
+    float bias = 0.f;
+    if (a.kbar) {
+        const float* kb = a.kbar + ((int64_t)b * a.Hkv + g) * D + hg * (D / 2);
+        float acc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            u32x4 raw = __builtin_bit_cast(u32x4, qf[kk]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc += E::to_float((uint16_t)(raw[j] & 0xffff)) * kb[kk * 8 + 2 * j];
+                acc += E::to_float((uint16_t)(raw[j] >> 16)) * kb[kk * 8 + 2 * j + 1];
+            }
+        }
+        acc += xor_shfl(acc, 32);
+        bias = acc * a.scale_log2;
+    }
+
+    // Keys this tile of rows can see.
+    int kv_end = Lk;
+    if (CAUSAL) kv_end = min(Lk, m0 + BM + Lk - Lq);
+    const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+    const int diag = Lk - Lq;  // row i sees keys j <= i + diag
+
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    u32x4 kr[NCH], vr[NCH];
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int ch = tid + c * 256;
+            const int key = ch / CPR, col = (ch % CPR) * 8;
+            const int j = t * BN + key;
+            u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
+            if (j < Lk) {
+                zk = load16(kp + (int64_t)j * a.kv_row + col);
+                zv = load16(vp + (int64_t)j * a.kv_row + col);
+            }
+            kr[c] = zk;
+            vr[c] = zv;
+        }
+    };
+
+    // Lane roles for the transpose read of V^T operands.
+    const int g16 = lane >> 4, e4 = (lane & 15) >> 2, q4 = lane & 3;
+
+    if (ntiles > 0) load_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+        __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int ch = tid + c * 256;
+            const int key = ch / CPR, col = (ch % CPR) * 8;
+            store16(&k_lds[key * KLD + col], kr[c]);
+            store16(&v_lds[key * VLD + col], vr[c]);
+        }
+        __syncthreads();
+        if (t + 1 < ntiles) load_tile(t + 1);
+
+        // S^T[key, row] for each 32-key block.
+        f32x16 s[NJB];
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+            s[jb] = f32x16{};
+            const uint16_t* kr0 = &k_lds[(jb * 32 + n) * KLD + hg * (D / 2)];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+                s[jb] = E::mfma32(as_vec8<T>(load16(kr0 + kk * 8)), qf[kk], s[jb]);
+        }
+
+        // scale, mask, running max (lane holds keys 8(i/4) + 4hg + i%4 of each block)
+        const int kbase = t * BN;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = kbase + jb * 32 + 8 * (i >> 2) + hg * 4 + (i & 3);
+                float x = s[jb][i] * a.scale_log2 - bias;
+                bool ok = key < Lk;
+                if (CAUSAL) ok = ok && key <= row + diag;
+                x = ok ? x : -INFINITY;
+                s[jb][i] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, xor_shfl(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        m_run = m_new;
+
+        // p = 2^(s - m), packed to 16-bit as the B operand of the PV product
+        uint32_t pk[NJB][2][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float p0 = fast_exp2(s[jb][8 * st + 2 * j] - m_use);
+                    const float p1 = fast_exp2(s[jb][8 * st + 2 * j + 1] - m_use);
+                    psum += p0 + p1;
+                    pk[jb][st][j] = E::pack2(p0, p1);
+                }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+
+        // O^T[d, row] += V^T[d, keys] P^T[keys, row]; k-step st of block jb covers
+        // keys 16st + 8h + 4(lane/32) + e for operand slots 4h + e.
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const int key0 = jb * 32 + 16 * st + 4 * (g16 >> 1) + e4;
+                    const int col = db * 32 + (g16 & 1) * 16 + 4 * q4;
+                    const u32x2 lo = lds_read_tr16(&v_lds[key0 * VLD + col]);
+                    const u32x2 hi = lds_read_tr16(&v_lds[(key0 + 8) * VLD + col]);
+                    const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
+                    const u32x4 bv = {pk[jb][st][0], pk[jb][st][1], pk[jb][st][2],
+                                      pk[jb][st][3]};
+                    o[db] = E::mfma32(as_vec8<T>(av), as_vec8<T>(bv), o[db]);
+                }
+    }
+
+    // Epilogue: out = O / l; LSE = m + log2(l) (+ smoothing bias), one store per row.
+    const float l_tot = l_run + xor_shfl(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (row_ok) {
+        uint16_t* op = (uint16_t*)a.out + q_off + (int64_t)h * a.q_head + (int64_t)row * a.q_row;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d = db * 32 + 8 * a4 + hg * 4;
+                u32x2 w;
+                w.x = E::pack2(o[db][4 * a4 + 0] * inv, o[db][4 * a4 + 1] * inv);
+                w.y = E::pack2(o[db][4 * a4 + 2] * inv, o[db][4 * a4 + 3] * inv);
+                *reinterpret_cast<u32x2*>(op + d) = w;
+            }
+        if (hg == 0 && a.lse)
+            a.lse[lse_off + (int64_t)h * a.lse_head + row] =
+                l_tot > 0.f ? m_run + fast_log2(l_tot) + bias : -INFINITY;
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_fmha_t(const FmhaArgs& a, bool causal, bool varlen, dim3 grid, hipStream_t st) {
+    const dim3 block(256);
+    if (causal) {
+        if (varlen)
+            hipLaunchKernelGGL((fmha_fwd_kernel<T, D, true, true>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((fmha_fwd_kernel<T, D, true, false>), grid, block, 0, st, a);
+    } else {
+        if (varlen)
+            hipLaunchKernelGGL((fmha_fwd_kernel<T, D, false, true>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((fmha_fwd_kernel<T, D, false, false>), grid, block, 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_fmha_d(const FmhaArgs& a, int D, bool causal, bool varlen, dim3 grid,
+                         hipStream_t st) {
+    switch (D) {
+        case 64: return launch_fmha_t<T, 64>(a, causal, varlen, grid, st);
+        case 128: return launch_fmha_t<T, 128>(a, causal, varlen, grid, st);
+        case 256: return launch_fmha_t<T, 256>(a, causal, varlen, grid, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int fmha_rows_per_block() { return FmhaTile<128>::BM; }
+
+hipError_t launch_fmha(const FmhaArgs& a, int dtype, int D, bool causal, bool varlen, int grid_m,
+                       int grid_b, hipStream_t stream) {
+    const dim3 grid((unsigned)grid_m, (unsigned)a.Hq, (unsigned)grid_b);
+    if (dtype == 0) return launch_fmha_d<__bf16>(a, D, causal, varlen, grid, stream);
+    return launch_fmha_d<_Float16>(a, D, causal, varlen, grid, stream);
+}
+
+}  // namespace skv

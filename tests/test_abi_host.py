@@ -1,0 +1,171 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry point,
+and rejects malformed arguments before touching the GPU."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (the HIP runtime torch ships must be the one libskv binds to)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skv.h")
+LIB = os.path.join(ROOT, "split_kv_merge_amd", "libskv.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(skv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libskv.so is not built (run __graft_entry__.build())")
+    import split_kv_merge_amd as skv
+    return skv._load()
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("skv_attn_fwd", "skv_attn_fwd_varlen", "skv_attn_splitkv_partial", "skv_merge_state"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), f"{name} declared in skv.h but not exported"
+
+
+def test_single_hip_runtime_mapped(lib):
+    maps = open("/proc/self/maps").read()
+    libs = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(libs) <= 1, libs
+
+
+def test_status_strings(lib):
+    assert lib.skv_status_str(0) == b"ok"
+    assert lib.skv_status_str(1) == b"invalid argument"
+    assert lib.skv_status_str(2) == b"unsupported configuration"
+
+
+def test_workspace_and_split_heuristic(lib):
+    assert lib.skv_workspace_bytes(2, 8, 128, 1) == 2 * 8 * 128 * 4
+    assert lib.skv_workspace_bytes(2, 8, 128, 0) == 0
+    for B, Hkv, Lkv in [(8, 8, 4096), (8, 8, 32768), (4, 4, 16384), (1, 1, 10), (1, 2, 0)]:
+        s = lib.skv_pick_num_splits(B, Hkv, 4, Lkv, 128)
+        assert 1 <= s <= max(1, Lkv // 128)
+
+
+# A fake but 256-byte aligned device-looking address: validation must reject the
+# call before any launch, so nothing ever dereferences it.
+FAKE = ctypes.c_void_p(0x10000)
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, D=128,
+             dtype=0, layout=0, scale=0.1, causal=0, smooth_k=0, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.skv_attn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                            a["Sq"], a["Sk"], a["D"], a["dtype"], a["layout"], a["scale"],
+                            a["causal"], a["smooth_k"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1),
+    (dict(Hq=6, Hkv=4), 1),           # not a multiple
+    (dict(Hkv=0), 1),
+    (dict(B=-1), 1),
+    (dict(Sq=-3), 1),
+    (dict(D=96), 2),                  # well-formed, not built
+    (dict(D=0), 1),
+    (dict(dtype=2), 2),               # fp32 attention not built
+    (dict(dtype=7), 1),
+    (dict(layout=5), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(scale=float("inf")), 1),
+    (dict(q=ctypes.c_void_p(0x10008)), 1),   # misaligned
+    (dict(smooth_k=1), 1),            # no workspace
+    (dict(smooth_k=1, ws=FAKE, ws_bytes=16), 1),  # too small
+])
+def test_attn_fwd_rejects(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+    assert lib.skv_last_error() != b""
+
+
+def test_zero_sized_calls_succeed_without_launching(lib):
+    assert _fwd(lib, B=0) == 0
+    assert _fwd(lib, Sq=0) == 0
+
+
+def test_varlen_rejects(lib):
+    P = FAKE
+
+    def call(**kw):
+        a = dict(nseq=2, total_q=10, total_k=10, maxq=8, Hq=4, Hkv=2, D=128, dtype=0, cu=P)
+        a.update(kw)
+        return lib.skv_attn_fwd_varlen(P, P, P, P, None, a["cu"], a["cu"], a["nseq"], a["total_q"],
+                                       a["total_k"], a["maxq"], a["Hq"], a["Hkv"], a["D"], a["dtype"],
+                                       0.1, 1, 0, None, 0, None)
+    assert call(cu=None) == 1
+    assert call(maxq=11) == 1
+    assert call(nseq=-1) == 1
+    assert call(Hq=5) == 1
+    assert call(D=48) == 2
+    assert call(nseq=0) == 0
+
+
+def test_splitkv_rejects(lib):
+    P = FAKE
+
+    def call(**kw):
+        a = dict(B=1, Hq=32, Hkv=8, Lq=1, Lkv=64, D=128, S=4)
+        a.update(kw)
+        return lib.skv_attn_splitkv_partial(P, P, P, P, P, a["B"], a["Hq"], a["Hkv"], a["Lq"],
+                                            a["Lkv"], a["D"], 0, 0, 0.1, a["S"], None)
+    assert call(S=0) == 1
+    assert call(Lq=0) == 1
+    assert call(Lkv=-1) == 1
+    assert call(Hq=30) == 1
+    assert call(Lq=5) == 2           # (32/8)*5 = 20 rows per kv head > 16
+    assert call(D=80) == 2
+    assert call(B=0) == 0
+
+
+def test_merge_rejects(lib):
+    P = FAKE
+    arr = ctypes.c_int64 * 3
+    good = arr(0, 128, 128)
+
+    def call(**kw):
+        a = dict(S=4, R=(1, 2, 3), D=128, pdt=2, odt=0, pstride=128 * 6, ps=good, ls=arr(0, 1, 1),
+                 os_=good)
+        a.update(kw)
+        return lib.skv_merge_state(a["S"], *a["R"], a["D"], P, a["pdt"], a["pstride"], a["ps"], P,
+                                   6, a["ls"], P, a["odt"], a["os_"], None, None, None)
+    assert call(S=0) == 1
+    assert call(R=(1, -2, 3)) == 1
+    assert call(D=100) == 2
+    assert call(pdt=9) == 1
+    assert call(pstride=3) == 1       # not a multiple of 16 bytes
+    assert call(ps=None) == 1
+    assert call(R=(0, 2, 3)) == 0     # no rows: nothing to do
+
+
+def test_python_binding_fails_loudly_without_gpu_tensors():
+    import split_kv_merge_amd as skv
+    q = torch.zeros(1, 2, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        skv.attn_fwd(q, q, q)
+
+
+def test_lse_varlen_to_dense_checks_shape():
+    import split_kv_merge_amd as skv
+    lse = torch.arange(2 * 6, dtype=torch.float32).reshape(2, 6)   # H=2, B=3, S=2
+    dense = skv.lse_varlen_to_dense(lse, 3, 2)
+    assert dense.shape == (3, 2, 2)
+    assert dense[1, 0, 1] == lse[0, 3]
+    with pytest.raises(ValueError):
+        skv.lse_varlen_to_dense(lse, 4, 2)
