@@ -1,0 +1,418 @@
+"""Benchmark of the split-KV decode step and the prefill forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Headline workload: split-KV decode with GQA, B=8, Hq=32, Hkv=8, Lq=1, D=128, bf16,
+HND, with Lkv = 4096, 8192 and 32768.  One step runs the decode (split-KV partials
++ merge) of all three problems back to back, each with the split count
+skv_pick_num_splits chooses; the 32768 problem (1.07 GB of K/V) evicts the
+256 MB Infinity Cache, so every problem of the next step reads cold HBM.  The
+step is captured once into a HIP graph and replayed; K replays are timed with
+torch.cuda.synchronize() on both sides.
+
+`value` = algorithmic bytes of a step (K + V + Q read, out + LSE written) / step
+time, in GB/s.  `roofline` covers the dominant kernel, splitkv_partial: its
+algorithmic bytes (K + V + Q) per launch over its average launch duration, timed
+with HIP events on the launch stream in a separate pass in which the launches are
+queued behind a spin kernel (so host overhead does not open gaps).
+`cpu_baseline` times the fp64 oracle (oracle/, C + OpenMP) on a bounded sample of
+the same workload.  `secondary` reports the other shapes of the same path
+(wide-head decode, varlen causal prefill, ring-style chunked prefill, the tiny
+LSE case) in us, GB/s or TFLOP/s and as a fraction of the roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 / fp16 MFMA, TFLOP/s
+METRIC = "split-KV decode µs & HBM GB/s (%peak); prefill TFLOP/s (%MFMA peak)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ helpers
+
+class Decode:
+    """One decode problem on the GPU with preallocated partial and output buffers."""
+
+    def __init__(self, skv, prob, num_splits=None):
+        self.skv = skv
+        self.host = prob
+        self.q, self.k, self.v = prob.q.cuda(), prob.k.cuda(), prob.v.cuda()
+        self.scale = prob.scale
+        B, Hq, Hkv, Lq, Lkv, D = prob.dims
+        self.dims = (B, Hq, Hkv, Lq, Lkv, D)
+        self.S = num_splits or skv.pick_num_splits(B, Hkv, (Hq // Hkv) * Lq, Lkv, D)
+        self.op = torch.empty((self.S, B, Hq, Lq, D), dtype=torch.float32, device="cuda")
+        self.lp = torch.empty((self.S, B, Hq, Lq), dtype=torch.float32, device="cuda")
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device="cuda")
+
+    def partial(self):
+        self.skv.attn_splitkv_partial(self.q, self.k, self.v, num_splits=self.S, scale=self.scale,
+                                      out_part=self.op, lse_part=self.lp)
+
+    def merge(self):
+        self.skv.merge_state(self.op, self.lp, out=self.out, lse=self.lse)
+
+    def step(self):
+        self.partial()
+        self.merge()
+
+    def kv_bytes(self):
+        B, Hq, Hkv, Lq, Lkv, D = self.dims
+        return 2 * B * Hkv * Lkv * D * 2
+
+    def partial_bytes(self):
+        """Algorithmic bytes of splitkv_partial: K + V + Q."""
+        B, Hq, Hkv, Lq, Lkv, D = self.dims
+        return self.kv_bytes() + B * Hq * Lq * D * 2
+
+    def step_bytes(self):
+        """Algorithmic bytes of the decode: K + V + Q read, out (16-bit) + LSE written."""
+        B, Hq, Hkv, Lq, Lkv, D = self.dims
+        return self.partial_bytes() + B * Hq * Lq * D * 2 + B * Hq * Lq * 4
+
+
+def capture(fn):
+    """Capture fn() (library calls only, all buffers preallocated) into a graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps, warm=3):
+    """Mean GPU time (us) of one replay, from HIP events around `reps` replays."""
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def _spin_cycles_per_ms():
+    """Calibrate torch.cuda._sleep (a spin kernel counting device clock cycles)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    torch.cuda._sleep(1_000_000)
+    e1.record()
+    torch.cuda.synchronize()
+    return 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
+
+
+def kernel_durations(launchers, reps):
+    """Per-launch GPU durations (us) of each callable, timed with HIP events on the
+    current (launch) stream.  The launches are queued behind a spin kernel that
+    outlasts the host's enqueue time, so host overhead cannot open idle gaps inside
+    a measured interval."""
+    n = len(launchers)
+    t0 = time.perf_counter()
+    for fn in launchers:            # one unmeasured pass: host enqueue cost
+        fn()
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - t0) * 1e3
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)] for _ in range(reps)]
+    cyc = _spin_cycles_per_ms()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(cyc * (3.0 * host_ms * reps + 5.0)))
+    for r in range(reps):
+        for i, fn in enumerate(launchers):
+            a, b = evs[r][i]
+            a.record()
+            fn()
+            b.record()
+    torch.cuda.synchronize()
+    return [sum(evs[r][i][0].elapsed_time(evs[r][i][1]) for r in range(reps)) * 1e3 / reps
+            for i in range(n)]
+
+
+# ------------------------------------------------------------- workloads
+
+def headline(skv, args):
+    import workloads as wl
+    lkvs = (4096, 8192, 32768)
+    dec = []
+    for L in lkvs:
+        log(f"generating decode_gqa Lkv={L}")
+        dec.append(Decode(skv, wl.decode_gqa(L)))
+
+    def step():
+        for d in dec:
+            d.step()
+
+    g = capture(step)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    step_bytes = sum(d.step_bytes() for d in dec)
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    # dominant kernel: splitkv_partial; durations per launch from HIP events
+    reps = max(5, min(args.steps, 20))
+    launchers = []
+    for d in dec:
+        launchers += [d.partial, d.merge]
+    durs = kernel_durations(launchers, reps)
+    part_us = [durs[2 * i] for i in range(len(dec))]
+    merge_us = [durs[2 * i + 1] for i in range(len(dec))]
+    avg_part_us = sum(part_us) / len(part_us)
+    avg_part_bytes = sum(d.partial_bytes() for d in dec) / len(dec)
+    achieved = avg_part_bytes / (avg_part_us * 1e-6) / 1e9
+
+    # per problem, from the same event pass (problems run in step order: cold HBM)
+    per = {}
+    for i, (L, d) in enumerate(zip(lkvs, dec)):
+        us = part_us[i] + merge_us[i]
+        gbs = d.step_bytes() / (us * 1e-6) / 1e9
+        per[str(L)] = dict(num_splits=d.S, partial_us=round(part_us[i], 2),
+                           merge_us=round(merge_us[i], 2), us=round(us, 2), gbs=round(gbs, 1),
+                           frac=round(gbs / HBM_PEAK_GBS, 4),
+                           partial_gbs=round(d.partial_bytes() / (part_us[i] * 1e-6) / 1e9, 1))
+    return dec, dict(ms=ms, value=value, step_bytes=step_bytes, achieved=achieved,
+                     avg_part_us=avg_part_us, avg_part_bytes=avg_part_bytes, per=per)
+
+
+def parity_sample(dec):
+    """A few rows of the measured decode problems against the oracle (sanity only)."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    errs = []
+    d = dec[0]
+    prob_q, prob_k, prob_v = d.host.q, d.host.k, d.host.v
+    B, Hq, Hkv, Lq, Lkv, D = d.dims
+    rows = np.array([[0, 0, 0], [B - 1, Hq - 1, Lq - 1], [B // 2, Hq // 3, 0]])
+    ro, rl = oracle.attn_rows(wl.bits(prob_q), wl.bits(prob_k), wl.bits(prob_v), "bf16", rows,
+                              scale=d.scale)
+    out, lse = d.out.float().cpu().numpy(), d.lse.cpu().numpy()
+    for n, (b, h, i) in enumerate(rows):
+        errs.append(max(abs(float(lse[b, h, i]) - rl[n]),
+                        float(np.abs(out[b, h, i] - ro[n]).max())))
+    return max(errs)
+
+
+def cpu_baseline(dec, args):
+    """The oracle's decode step (fp64 per-chunk partials + merge, same split counts) on
+    the same three problems, repeated until at least 10 s of host time has passed."""
+    import oracle
+    import workloads as wl
+    cores = len(os.sched_getaffinity(0))
+    threads = min(int(os.environ.get("OMP_NUM_THREADS", cores)), cores)
+    inputs = [(wl.bits(d.host.q), wl.bits(d.host.k), wl.bits(d.host.v), d) for d in dec]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for qb, kb, vb, d in inputs:
+            o, l = oracle.splitkv_partials(qb, kb, vb, "bf16", d.S, scale=d.scale)
+            oracle.merge(o, l)
+        reps += 1
+        sec = time.perf_counter() - t0
+        if sec >= 10.0 or sec * (reps + 1) / reps > 30.0:
+            break
+    step_bytes = sum(d.step_bytes() for d in dec)
+    return dict(value=round(step_bytes * reps / sec / 1e9, 4), unit="GB/s", cores=threads,
+                kind="oracle",
+                sample=f"the whole decode step (Lkv 4096, 8192, 32768; B=8 Hq=32 Hkv=8 D=128), "
+                       f"fp64 partials + merge, {reps} repetition(s) in {sec:.1f} s",
+                cpu=platform.processor() or platform.machine())
+
+
+def secondary(skv, args):
+    import workloads as wl
+    res = {}
+    reps = 20
+
+    # wide-head decode: B4 Hq16 Hkv4 Lq4 D256, K offset +2; the two problems
+    # alternate, so each reads what the other evicted
+    wides = []
+    for L in (16384, 32768):
+        log(f"generating wide_decode Lkv={L}")
+        wides.append((L, Decode(skv, wl.wide_decode(L, +1))))
+    launchers = []
+    for _, d in wides:
+        launchers += [d.partial, d.merge]
+    durs = kernel_durations(launchers, reps)
+    for i, (L, d) in enumerate(wides):
+        us = durs[2 * i] + durs[2 * i + 1]
+        gbs = d.step_bytes() / (us * 1e-6) / 1e9
+        res[f"decode_wide_D256_Lq4_Lkv{L}"] = dict(
+            us=round(us, 2), partial_us=round(durs[2 * i], 2), merge_us=round(durs[2 * i + 1], 2),
+            gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4), num_splits=d.S)
+    del wides, launchers
+    torch.cuda.empty_cache()
+
+    # varlen causal prefill: 16 sequences, lengths U[128, 4096], Hq32 Hkv8 D128 bf16
+    log("generating varlen_prefill")
+    vl = wl.varlen_prefill(seed=4)
+    q, k, v = vl.q.cuda(), vl.k.cuda(), vl.v.cuda()
+    cq, ck = vl.cu_seqlens_q.cuda(), vl.cu_seqlens_k.cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
+    mx = max(vl.lengths)
+
+    def varlen():
+        skv.attn_fwd_varlen(q, k, v, cq, ck, mx, scale=vl.scale, causal=True, out=out, lse=lse)
+    us = time_graph(capture(varlen), reps)
+    fl = wl.prefill_flops(vl.lengths, 32, 128, causal=True)
+    tf = fl / (us * 1e-6) / 1e12
+    res["prefill_varlen_causal_16seq_Hq32_Hkv8_D128"] = dict(
+        us=round(us, 1), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4),
+        total_tokens=vl.meta["T"], flop=fl)
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+
+    # ring-style chunked prefill: B1 H16 S8192 D64 fp16, 4 KV chunks with smoothing + merge
+    log("generating ring_chunks")
+    rc = wl.ring_chunks(seed=5)
+    q = rc["q"].cuda()
+    kc = [t.cuda() for t in rc["k_chunks"]]
+    vc = [t.cuda() for t in rc["v_chunks"]]
+    kf, vf = rc["k"].cuda(), rc["v"].cuda()
+    po = torch.empty((4,) + tuple(q.shape), dtype=q.dtype, device="cuda")
+    pl = torch.empty((4, 1, 16, 8192), dtype=torch.float32, device="cuda")
+    mo = torch.empty_like(q)
+    ml = torch.empty((1, 16, 8192), dtype=torch.float32, device="cuda")
+    fo = torch.empty_like(q)
+    fl_ = torch.empty((1, 16, 8192), dtype=torch.float32, device="cuda")
+
+    def ring():
+        for c in range(4):
+            skv.attn_fwd(q, kc[c], vc[c], scale=rc["scale"], smooth_k=True, out=po[c], lse=pl[c])
+        skv.merge_state(po, pl, out=mo, lse=ml)
+
+    def full():
+        skv.attn_fwd(q, kf, vf, scale=rc["scale"], out=fo, lse=fl_)
+    fl = 4 * 16 * 8192 * 8192 * 64
+    for name, fn in (("prefill_ring_4chunks_smooth_merge_H16_S8192_D64_fp16", ring),
+                     ("prefill_full_H16_S8192_D64_fp16", full)):
+        us = time_graph(capture(fn), reps)
+        tf = fl / (us * 1e-6) / 1e12
+        res[name] = dict(us=round(us, 1), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4),
+                         flop=fl)
+    # tiny LSE case: B1 H4 Sq64 Sk1000 D128 bf16 (launch-bound)
+    d = wl.tiny_lse()
+    tq, tk, tv = d["q_rows"].cuda(), d["k"].cuda(), d["v"].cuda()
+    to = torch.empty_like(tq)
+    tl = torch.empty((1, 4, 64), dtype=torch.float32, device="cuda")
+
+    def tiny():
+        skv.attn_fwd(tq, tk, tv, scale=d["scale"], out=to, lse=tl)
+    res["tiny_lse_B1_H4_Sq64_Sk1000_D128"] = dict(us=round(time_graph(capture(tiny), reps), 2))
+    return res
+
+
+def copy_probe():
+    """A plain device copy of known size (256 MiB read + 256 MiB written), for
+    scaling the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
+    a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import split_kv_merge_amd as skv
+    skv._load()
+    torch.cuda.init()
+    dec, h = headline(skv, args)
+    err = parity_sample(dec)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(dec, args)
+    sec = {} if args.no_secondary else secondary(skv, args)
+    copy_probe()
+    line = {
+        "metric": METRIC,
+        "value": round(h["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_gqa: split-KV partials + merge, B=8 Hq=32 Hkv=8 Lq=1 D=128 bf16 HND, "
+                        "Lkv 4096 + 8192 + 32768 per step",
+            "global_batch": 8,
+            "seq_len": [4096, 8192, 32768],
+            "parallelism": "single GPU",
+            "num_splits": {k: v["num_splits"] for k, v in h["per"].items()},
+            "step_bytes": h["step_bytes"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(h["achieved"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "splitkv_partial (bf16, D=128)",
+            "avg_launch_us": round(h["avg_part_us"], 2),
+            "algorithmic_bytes_per_launch": int(h["avg_part_bytes"]),
+        },
+        "cpu_baseline": cpu,
+        "per_problem": h["per"],
+        "parity_sample_max_err": round(err, 5),
+        "secondary": sec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
