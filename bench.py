@@ -11,10 +11,13 @@ step is captured once into a HIP graph and replayed; K replays are timed with
 torch.cuda.synchronize() on both sides.
 
 `value` = algorithmic bytes of a step (K + V + Q read, out + LSE written) / step
-time, in GB/s.  `roofline` covers the dominant kernel, splitkv_partial: its
-algorithmic bytes (K + V + Q) per launch over its average launch duration, timed
-with HIP events on the launch stream in a separate pass in which the launches are
-queued behind a spin kernel (so host overhead does not open gaps).
+time, in GB/s.  The decode runs as skv_attn_splitkv_decode: one launch computes
+the per-chunk partial states and the last work group of each (batch, kv head)
+merges them.  `roofline` covers that kernel: its algorithmic bytes per launch over
+its average launch duration, timed with HIP events on the launch stream in a
+separate pass in which the launches are queued behind a spin kernel (so host
+overhead does not open gaps).  The two-kernel form (partials, then merge_state)
+is timed as well and reported per problem.
 `cpu_baseline` times the fp64 oracle (oracle/, C + OpenMP) on a bounded sample of
 the same workload.  `secondary` reports the other shapes of the same path
 (wide-head decode, varlen causal prefill, ring-style chunked prefill, the tiny
@@ -71,6 +74,8 @@ class Decode:
         self.lp = torch.empty((self.S, B, Hq, Lq), dtype=torch.float32, device="cuda")
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device="cuda")
+        self.ws = torch.zeros(skv.splitkv_workspace_bytes(B, Hq, Lq, D, self.S, Hkv),
+                              dtype=torch.uint8, device="cuda")
 
     def partial(self):
         self.skv.attn_splitkv_partial(self.q, self.k, self.v, num_splits=self.S, scale=self.scale,
@@ -79,16 +84,21 @@ class Decode:
     def merge(self):
         self.skv.merge_state(self.op, self.lp, out=self.out, lse=self.lse)
 
-    def step(self):
+    def two_kernel(self):
         self.partial()
         self.merge()
+
+    def step(self):
+        """Single-launch decode: partials + in-kernel merge."""
+        self.skv.attn_splitkv_decode(self.q, self.k, self.v, num_splits=self.S, scale=self.scale,
+                                     out=self.out, lse=self.lse, workspace=self.ws)
 
     def kv_bytes(self):
         B, Hq, Hkv, Lq, Lkv, D = self.dims
         return 2 * B * Hkv * Lkv * D * 2
 
     def partial_bytes(self):
-        """Algorithmic bytes of splitkv_partial: K + V + Q."""
+        """Algorithmic bytes of the partial pass alone: K + V + Q."""
         B, Hq, Hkv, Lq, Lkv, D = self.dims
         return self.kv_bytes() + B * Hq * Lq * D * 2
 
@@ -193,29 +203,32 @@ def headline(skv, args):
     step_bytes = sum(d.step_bytes() for d in dec)
     value = step_bytes / (ms * 1e-3) / 1e9
 
-    # dominant kernel: splitkv_partial; durations per launch from HIP events
+    # dominant kernel: the single-launch decode kernel (all of the step's work);
+    # durations per launch from HIP events.  The two-kernel form (partials, then
+    # merge_state) is timed too, for comparison.
     reps = max(5, min(args.steps, 20))
+    fused_us = kernel_durations([d.step for d in dec], reps)
     launchers = []
     for d in dec:
         launchers += [d.partial, d.merge]
     durs = kernel_durations(launchers, reps)
     part_us = [durs[2 * i] for i in range(len(dec))]
     merge_us = [durs[2 * i + 1] for i in range(len(dec))]
-    avg_part_us = sum(part_us) / len(part_us)
-    avg_part_bytes = sum(d.partial_bytes() for d in dec) / len(dec)
-    achieved = avg_part_bytes / (avg_part_us * 1e-6) / 1e9
+    avg_us = sum(fused_us) / len(fused_us)
+    avg_bytes = sum(d.step_bytes() for d in dec) / len(dec)
+    achieved = avg_bytes / (avg_us * 1e-6) / 1e9
 
-    # per problem, from the same event pass (problems run in step order: cold HBM)
+    # per problem, from the same event passes (problems run in step order: cold HBM)
     per = {}
     for i, (L, d) in enumerate(zip(lkvs, dec)):
-        us = part_us[i] + merge_us[i]
+        us = fused_us[i]
         gbs = d.step_bytes() / (us * 1e-6) / 1e9
-        per[str(L)] = dict(num_splits=d.S, partial_us=round(part_us[i], 2),
-                           merge_us=round(merge_us[i], 2), us=round(us, 2), gbs=round(gbs, 1),
+        per[str(L)] = dict(num_splits=d.S, us=round(us, 2), gbs=round(gbs, 1),
                            frac=round(gbs / HBM_PEAK_GBS, 4),
-                           partial_gbs=round(d.partial_bytes() / (part_us[i] * 1e-6) / 1e9, 1))
+                           two_kernel_us=round(part_us[i] + merge_us[i], 2),
+                           partial_us=round(part_us[i], 2), merge_us=round(merge_us[i], 2))
     return dec, dict(ms=ms, value=value, step_bytes=step_bytes, achieved=achieved,
-                     avg_part_us=avg_part_us, avg_part_bytes=avg_part_bytes, per=per)
+                     avg_us=avg_us, avg_bytes=avg_bytes, per=per)
 
 
 def parity_sample(dec):
@@ -274,16 +287,14 @@ def secondary(skv, args):
     for L in (16384, 32768):
         log(f"generating wide_decode Lkv={L}")
         wides.append((L, Decode(skv, wl.wide_decode(L, +1))))
-    launchers = []
-    for _, d in wides:
-        launchers += [d.partial, d.merge]
+    launchers = [d.step for _, d in wides]
     durs = kernel_durations(launchers, reps)
     for i, (L, d) in enumerate(wides):
-        us = durs[2 * i] + durs[2 * i + 1]
+        us = durs[i]
         gbs = d.step_bytes() / (us * 1e-6) / 1e9
         res[f"decode_wide_D256_Lq4_Lkv{L}"] = dict(
-            us=round(us, 2), partial_us=round(durs[2 * i], 2), merge_us=round(durs[2 * i + 1], 2),
-            gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4), num_splits=d.S)
+            us=round(us, 2), gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
+            num_splits=d.S)
     del wides, launchers
     torch.cuda.empty_cache()
 
@@ -387,8 +398,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "decode_gqa: split-KV partials + merge, B=8 Hq=32 Hkv=8 Lq=1 D=128 bf16 HND, "
-                        "Lkv 4096 + 8192 + 32768 per step",
+            "workload": "decode_gqa: split-KV decode (partials + stable merge, one launch), "
+                        "B=8 Hq=32 Hkv=8 Lq=1 D=128 bf16 HND, Lkv 4096 + 8192 + 32768 per step",
             "global_batch": 8,
             "seq_len": [4096, 8192, 32768],
             "parallelism": "single GPU",
@@ -402,9 +413,9 @@ def main():
             "unit": "GB/s",
             "frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "kernel": "splitkv_partial (bf16, D=128)",
-            "avg_launch_us": round(h["avg_part_us"], 2),
-            "algorithmic_bytes_per_launch": int(h["avg_part_bytes"]),
+            "kernel": "splitkv_kernel<bf16, 128, single-launch> (skv_attn_splitkv_decode)",
+            "avg_launch_us": round(h["avg_us"], 2),
+            "algorithmic_bytes_per_launch": int(h["avg_bytes"]),
         },
         "cpu_baseline": cpu,
         "per_problem": h["per"],

@@ -134,6 +134,33 @@ skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* 
                                       void* stream);
 
 /*
+ * Split-KV decode in one launch: the partial states of skv_attn_splitkv_partial
+ * followed by their stable merge (as skv_merge_state computes it), done by the
+ * last work group of each (batch, kv head) to finish [ET description: stable
+ * per-split softmax and global-max rescale; reviewer item 2: keep the reduce off
+ * a separate serial path].
+ *
+ *   q, k, v, layout, num_splits: as skv_attn_splitkv_partial; num_splits <= 256
+ *       (SKV_EUNSUPPORTED beyond).
+ *   out  q's shape, layout and dtype: the merged output.
+ *   lse  float32 [B, Hq, Lq] (log2) or NULL.
+ *   workspace: device memory of skv_splitkv_workspace_bytes(B, Hq, Lq, D,
+ *       num_splits, Hkv) bytes, 256-byte aligned, holding the partial states and one
+ *       arrival counter per (batch, kv head).  It must be ZERO-FILLED before its
+ *       first use; every call returns the counters to zero, so one zero fill serves
+ *       any number of later calls (including HIP graph replays).  Two calls that
+ *       may run at the same time must not share a workspace.
+ */
+skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v, void* out,
+                                     float* lse, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                                     skv_dtype_t dtype, skv_layout_t layout, float scale,
+                                     int num_splits, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/* Workspace bytes of skv_attn_splitkv_decode (0 for non-positive sizes). */
+size_t skv_splitkv_workspace_bytes(int B, int Hq, int Lq, int D, int num_splits, int Hkv);
+
+/*
  * Stable merge of num_parts partial states (o_s, lse_s) per row [ET Copilot
  * overview: global max over splits, rescale each split, reduce all together;
  * reviewer item 2: keep the exponentials off a serial chain, parallelise over D].
@@ -168,9 +195,9 @@ skv_status_t skv_merge_state(int num_parts, int R0, int R1, int R2, int D,
  * buffer [B_or_nseq, Hkv, D] when smooth_k != 0, else 0. */
 size_t skv_workspace_bytes(int B_or_nseq, int Hkv, int D, int smooth_k);
 
-/* A split count for skv_attn_splitkv_partial: enough (batch, kv head, chunk) work
- * groups to cover the 256 compute units several times, with chunks of at least a
- * few 32-key blocks.  Pure host arithmetic; returns >= 1. */
+/* A split count for the split-KV calls: about one or two (batch, kv head, chunk)
+ * work groups per compute unit (256 CUs), with chunks of at least 256 keys.  Pure
+ * host arithmetic; returns >= 1. */
 int skv_pick_num_splits(int B, int Hkv, int rows_per_kv_head, int Lkv, int D);
 
 /* Static description of a status code. */

@@ -8,8 +8,9 @@ Every step of the computation runs in the library's kernels.  There is no CPU
 fallback: if the library is missing, every call raises.
 
 Functions (same names as the C entry points without the ``skv_`` prefix):
-    attn_fwd, attn_fwd_varlen, attn_splitkv_partial, merge_state,
-    workspace_bytes, pick_num_splits, lse_varlen_to_dense
+    attn_fwd, attn_fwd_varlen, attn_splitkv_partial, attn_splitkv_decode,
+    merge_state, workspace_bytes, splitkv_workspace_bytes, pick_num_splits,
+    lse_varlen_to_dense
 """
 from __future__ import annotations
 
@@ -18,8 +19,9 @@ import os
 
 import torch
 
-__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_splitkv_partial", "merge_state",
-           "workspace_bytes", "pick_num_splits", "lse_varlen_to_dense", "SkvError", "lib_path"]
+__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_splitkv_partial", "attn_splitkv_decode",
+           "merge_state", "workspace_bytes", "splitkv_workspace_bytes", "pick_num_splits",
+           "lse_varlen_to_dense", "SkvError", "lib_path"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libskv.so")
@@ -59,6 +61,10 @@ def _load():
     lib.skv_attn_fwd_varlen.restype = I
     lib.skv_attn_splitkv_partial.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
     lib.skv_attn_splitkv_partial.restype = I
+    lib.skv_attn_splitkv_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
+    lib.skv_attn_splitkv_decode.restype = I
+    lib.skv_splitkv_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.skv_splitkv_workspace_bytes.restype = SZ
     lib.skv_merge_state.argtypes = [I, I, I, I, I, P, I, I64, I64P, P, I64, I64P, P, I, I64P, P, I64P, P]
     lib.skv_merge_state.restype = I
     lib.skv_workspace_bytes.argtypes = [I, I, I, I]
@@ -250,6 +256,55 @@ def attn_splitkv_partial(q, k, v, num_splits=None, scale=None, layout="HND", out
                                         SKV_HND if layout == "HND" else SKV_NHD, float(scale), S,
                                         _stream(q.device)))
     return out_part, lse_part
+
+
+def splitkv_workspace_bytes(B: int, Hq: int, Lq: int, D: int, num_splits: int, Hkv: int) -> int:
+    return int(_load().skv_splitkv_workspace_bytes(B, Hq, Lq, D, num_splits, Hkv))
+
+
+def attn_splitkv_decode(q, k, v, num_splits=None, scale=None, layout="HND", out=None, lse=None,
+                        workspace=None, return_lse=True):
+    """Split-KV decode in one launch (partials + stable merge): returns (out, lse) with
+    out in q's shape and dtype and lse float32 [B, Hq, Lq] (log2).
+
+    ``workspace`` (uint8 GPU tensor of splitkv_workspace_bytes(...) bytes) must be
+    zero-filled before its first use; the call leaves it zero-filled again, so it can
+    be reused by later calls and graph replays.  A fresh zeroed one is made if None.
+    """
+    lib = _load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda_contig(n, t)
+    if v.shape != k.shape or q.dtype != k.dtype or v.dtype != k.dtype:
+        raise ValueError("k and v must match in shape, and q, k, v in dtype")
+    B, Hq, Hkv, Lq, Lkv, D = _dims(q, k, layout)
+    if Hkv <= 0 or Hq % Hkv:
+        raise ValueError(f"Hq ({Hq}) must be a multiple of Hkv ({Hkv})")
+    if num_splits is None:
+        num_splits = pick_num_splits(B, Hkv, (Hq // Hkv) * Lq, Lkv, D)
+    if scale is None:
+        scale = D ** -0.5
+    S = int(num_splits)
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda_contig("out", out)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need_cuda_contig("lse", lse)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Lq):
+            raise ValueError(f"lse must be float32 {(B, Hq, Lq)}")
+    need = splitkv_workspace_bytes(B, Hq, Lq, D, S, Hkv)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need_cuda_contig("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.skv_attn_splitkv_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv,
+                                       Lq, Lkv, D, _dt(q), SKV_HND if layout == "HND" else SKV_NHD,
+                                       float(scale), S, _ptr(workspace), ws_bytes,
+                                       _stream(q.device)))
+    return (out, lse) if lse is not None else out
 
 
 def _rows3(t: torch.Tensor, lead: int, tail: int):

@@ -90,14 +90,15 @@ size_t skv_workspace_bytes(int B_or_nseq, int Hkv, int D, int smooth_k) {
 
 int skv_pick_num_splits(int B, int Hkv, int rows_per_kv_head, int Lkv, int D) {
     (void)rows_per_kv_head;
-    (void)D;
     if (B <= 0 || Hkv <= 0 || Lkv <= 0) return 1;
-    // Aim for ~4 work groups per compute unit (256 CUs) while keeping at least
-    // 128 keys (one 32-key block per wave) in every chunk.
+    // One or two work groups per compute unit (256 CUs) stream best: each then
+    // keeps several blocks in flight per wave, and a launch needs a single round of
+    // work groups.  Wide heads (D = 256) carry twice the bytes per key and do best
+    // with one.  Every chunk keeps at least 256 keys (two 32-key blocks per wave).
     const int64_t units = (int64_t)B * Hkv;
-    const int64_t target = 1024;
+    const int64_t target = D >= 256 ? 256 : 512;
     int64_t s = (target + units - 1) / units;
-    int64_t smax = Lkv / 128;
+    int64_t smax = Lkv / 256;
     if (smax < 1) smax = 1;
     if (s > smax) s = smax;
     if (s > 256) s = 256;
@@ -218,14 +219,15 @@ skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
     return launched(skv::launch_fmha(a, dtype, D, causal != 0, true, grid_m, nseq, s), "fmha_fwd_varlen");
 }
 
-skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* v,
-                                      float* out_part, float* lse_part, int B, int Hq,
-                                      int Hkv, int Lq, int Lkv, int D, skv_dtype_t dtype,
-                                      skv_layout_t layout, float scale, int num_splits,
-                                      void* stream) {
-    clear_err();
-    if (!q || !out_part || !lse_part)
-        return fail(SKV_EINVAL, "q, out_part and lse_part must be non-NULL");
+}  // extern "C"
+
+namespace {
+
+// Validation and argument block shared by the two split-KV entry points.
+skv_status_t prepare_split(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                           int Lq, int Lkv, int D, skv_dtype_t dtype, skv_layout_t layout,
+                           float scale, int num_splits, skv::SplitArgs& a) {
+    if (!q) return fail(SKV_EINVAL, "q must be non-NULL");
     if ((!k || !v) && Lkv > 0) return fail(SKV_EINVAL, "k and v must be non-NULL when Lkv > 0");
     if (B < 0 || Lq < 1 || Lkv < 0)
         return fail(SKV_EINVAL, "need B >= 0, Lq >= 1, Lkv >= 0 (B=%d, Lq=%d, Lkv=%d)", B, Lq, Lkv);
@@ -237,17 +239,14 @@ skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* 
     if ((int64_t)(Hq / Hkv) * Lq > 16)
         return fail(SKV_EUNSUPPORTED, "(Hq/Hkv)*Lq = %lld query rows per kv head exceeds 16",
                     (long long)(Hq / Hkv) * Lq);
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out_part, 16))
-        return fail(SKV_EINVAL, "q, k, v and out_part must be 16-byte aligned");
-    if (!aligned(lse_part, 4)) return fail(SKV_EINVAL, "lse_part must be 4-byte aligned");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return fail(SKV_EINVAL, "q, k and v must be 16-byte aligned");
     if (B > 65535 || Hkv > 65535) return fail(SKV_EUNSUPPORTED, "B or Hkv exceeds the 65535 grid limit");
     if (!elems_ok({num_splits, B, Hq, Lq, D}) || !elems_ok({B, Hkv, Lkv, D}))
         return fail(SKV_EINVAL, "tensor sizes overflow 64-bit indexing");
-    if (B == 0) return SKV_OK;
-
     const bool hnd = layout == SKV_HND;
-    skv::SplitArgs a{};
-    a.q = q; a.k = k; a.v = v; a.out_part = out_part; a.lse_part = lse_part;
+    a = skv::SplitArgs{};
+    a.q = q; a.k = k; a.v = v;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lkv = Lkv; a.num_splits = num_splits;
     a.q_row = hnd ? D : (int64_t)Hq * D;
     a.q_head = hnd ? (int64_t)Lq * D : D;
@@ -257,7 +256,71 @@ skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* 
     a.kv_batch = (int64_t)Hkv * Lkv * D;
     a.part_stride = (int64_t)B * Hq * Lq * D;
     a.scale_log2 = scale * 1.4426950408889634f;
-    return launched(skv::launch_splitkv(a, dtype, D, (hipStream_t)stream), "splitkv_partial");
+    return SKV_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* v,
+                                      float* out_part, float* lse_part, int B, int Hq,
+                                      int Hkv, int Lq, int Lkv, int D, skv_dtype_t dtype,
+                                      skv_layout_t layout, float scale, int num_splits,
+                                      void* stream) {
+    clear_err();
+    if (!out_part || !lse_part) return fail(SKV_EINVAL, "out_part and lse_part must be non-NULL");
+    skv::SplitArgs a;
+    skv_status_t st = prepare_split(q, k, v, B, Hq, Hkv, Lq, Lkv, D, dtype, layout, scale,
+                                    num_splits, a);
+    if (st != SKV_OK) return st;
+    if (!aligned(out_part, 16)) return fail(SKV_EINVAL, "out_part must be 16-byte aligned");
+    if (!aligned(lse_part, 4)) return fail(SKV_EINVAL, "lse_part must be 4-byte aligned");
+    if (B == 0) return SKV_OK;
+    a.out_part = out_part;
+    a.lse_part = lse_part;
+    return launched(skv::launch_splitkv(a, dtype, D, false, (hipStream_t)stream), "splitkv_partial");
+}
+
+size_t skv_splitkv_workspace_bytes(int B, int Hq, int Lq, int D, int num_splits, int Hkv) {
+    if (B <= 0 || Hq <= 0 || Lq <= 0 || D <= 0 || num_splits <= 0 || Hkv <= 0) return 0;
+    const size_t rows = (size_t)num_splits * B * Hq * Lq;
+    return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float)) +
+           align256((size_t)B * Hkv * sizeof(int));
+}
+
+skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v, void* out,
+                                     float* lse, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                                     skv_dtype_t dtype, skv_layout_t layout, float scale,
+                                     int num_splits, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    clear_err();
+    if (!out) return fail(SKV_EINVAL, "out must be non-NULL");
+    skv::SplitArgs a;
+    skv_status_t st = prepare_split(q, k, v, B, Hq, Hkv, Lq, Lkv, D, dtype, layout, scale,
+                                    num_splits, a);
+    if (st != SKV_OK) return st;
+    if (!aligned(out, 16)) return fail(SKV_EINVAL, "out must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(SKV_EINVAL, "lse must be 4-byte aligned");
+    if (num_splits > skv::kMaxDecodeSplits)
+        return fail(SKV_EUNSUPPORTED, "the single-launch decode takes at most %d splits (got %d)",
+                    skv::kMaxDecodeSplits, num_splits);
+    const size_t need = skv_splitkv_workspace_bytes(B, Hq, Lq, D, num_splits, Hkv);
+    if (B > 0 && (!workspace || !aligned(workspace, 256)))
+        return fail(SKV_EINVAL, "the decode workspace must be non-NULL and 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(SKV_EINVAL, "workspace has %zu bytes, the decode needs %zu", workspace_bytes, need);
+    if (B == 0) return SKV_OK;
+    const size_t rows = (size_t)num_splits * B * Hq * Lq;
+    char* ws = (char*)workspace;
+    a.out_part = (float*)ws;
+    a.lse_part = (float*)(ws + align256(rows * D * sizeof(float)));
+    a.ticket = (int*)(ws + align256(rows * D * sizeof(float)) + align256(rows * sizeof(float)));
+    a.out = out;
+    a.lse = lse;
+    return launched(skv::launch_splitkv(a, dtype, D, true, (hipStream_t)stream), "splitkv_decode");
 }
 
 skv_status_t skv_merge_state(int num_parts, int R0, int R1, int R2, int D,

@@ -126,20 +126,18 @@ __global__ __launch_bounds__(256) void fmha_fwd_kernel(FmhaArgs a) {
     for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
+    // K/V tile loads.  Rows past the last key are clamped to it (real, finite data;
+    // a tile exists only when Lk > 0) and masked out of the softmax, so no load
+    // needs a branch.
     u32x4 kr[NCH], vr[NCH];
     auto load_tile = [&](int t) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int ch = tid + c * 256;
             const int key = ch / CPR, col = (ch % CPR) * 8;
-            const int j = t * BN + key;
-            u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-            if (j < Lk) {
-                zk = load16(kp + (int64_t)j * a.kv_row + col);
-                zv = load16(vp + (int64_t)j * a.kv_row + col);
-            }
-            kr[c] = zk;
-            vr[c] = zv;
+            const int j = min(t * BN + key, Lk - 1);
+            kr[c] = load16(kp + (int64_t)j * a.kv_row + col);
+            vr[c] = load16(vp + (int64_t)j * a.kv_row + col);
         }
     };
 

@@ -46,6 +46,11 @@ struct SplitArgs {
     int64_t kv_row, kv_head, kv_batch;
     int64_t part_stride;        // elements between consecutive splits of out_part
     float scale_log2;
+    // single-launch decode only: merged output (q's dtype and strides), its LSE
+    // [B, Hq, Lq] (nullable) and one arrival ticket per (batch, kv head)
+    void* out;
+    float* lse;
+    int* ticket;
 };
 
 // Merge of partial states over rows (r0, r1, r2).
@@ -67,7 +72,8 @@ hipError_t launch_fmha(const FmhaArgs& a, int dtype, int D, bool causal, bool va
                        int grid_m, int grid_b, hipStream_t stream);
 hipError_t launch_kmean(const KmeanArgs& a, int dtype, int D, bool varlen, int grid_b,
                         hipStream_t stream);
-hipError_t launch_splitkv(const SplitArgs& a, int dtype, int D, hipStream_t stream);
+constexpr int kMaxDecodeSplits = 256;  // single-launch decode: its merge keeps R x S weights in LDS
+hipError_t launch_splitkv(const SplitArgs& a, int dtype, int D, bool fused, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int parts_dtype, int out_dtype, int D,
                         hipStream_t stream);
 

@@ -8,11 +8,9 @@
 // and the weighted sum is spread over the head dimension, so no exponential sits
 // on a loop-carried chain.
 //
-// Layout: a row is handled by D/VEC lanes, each owning VEC contiguous elements
-// (one 16-byte load per part); a wave covers 64/(D/VEC) rows and a work group 4
-// waves.  The max pass strides the parts over the row's lanes and reduces with
-// xor shuffles inside the row's lane group; every lane then walks all parts,
-// reading each lse_s as a broadcast and accumulating w_s * o_s for its slice.
+// Layout: a part-group of D/VEC lanes covers one row's head dimension, each lane
+// owning VEC contiguous elements (one 16-byte load per part); several part-groups
+// share a row so that the parts of one row are read in parallel.
 #include "device.h"
 #include "launch.h"
 
@@ -75,51 +73,94 @@ template <typename TO, int VEC> struct OutStore {
     }
 };
 
+// A row's parts are split over P part-groups of LPR = D/VEC lanes each; T = P * LPR
+// lanes serve one row (a power of two, at most 256), 256 / T rows per block.
+//   1. max: the row's lanes load the partial LSEs in parallel (lane t takes parts
+//      t, t + T, ...), reduce with xor shuffles inside the wave and, when a row
+//      spans several waves, through LDS;
+//   2. lane (pg, sub) accumulates w_s * o_s over parts s = pg, pg + P, ... for its
+//      VEC elements, w_s = 2^(lse_s - M);
+//   3. the P partial sums of a row are added through LDS by part-group 0.
 template <typename TP, typename TO, int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int P) {
     constexpr int VEC = PartLoad<TP>::VEC;
-    constexpr int LPR = D / VEC;   // lanes per row
-    constexpr int RPW = 64 / LPR;  // rows per wave
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int sub = lane % LPR;
-    const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * RPW + lane / LPR;
-    if (row >= a.rows) return;  // whole lane groups leave together
+    constexpr int LPR = D / VEC;  // lanes per part-group
+    __shared__ __attribute__((aligned(16))) float red[256 * (VEC + 1)];
+    __shared__ float wmax[4];
 
-    const int64_t r2 = row % a.R2, r1 = (row / a.R2) % a.R1, r0 = row / ((int64_t)a.R1 * a.R2);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int T = LPR * P;        // lanes per row
+    const int rib = tid / T, t = tid % T, pg = t / LPR, sub = t % LPR;
+    const int64_t row = (int64_t)blockIdx.x * (256 / T) + rib;
+    const bool live = row < a.rows;
+
+    int64_t r0 = 0, r1 = 0, r2 = 0;
+    if (live) {
+        r2 = row % a.R2;
+        r1 = (row / a.R2) % a.R1;
+        r0 = row / ((int64_t)a.R1 * a.R2);
+    }
     const float* lp = a.parts_lse + r0 * a.pl_s0 + r1 * a.pl_s1 + r2 * a.pl_s2;
     const TP* op = (const TP*)a.parts_out + r0 * a.po_s0 + r1 * a.po_s1 + r2 * a.po_s2 + sub * VEC;
 
-    // pass 1: global max of the partial LSEs
+    // 1. row max of the partial LSEs
     float M = -INFINITY;
-    for (int s = sub; s < a.num_parts; s += LPR) M = fmaxf(M, lp[(int64_t)s * a.pl_part]);
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) M = fmaxf(M, xor_shfl(M, off));
+    if (live)
+        for (int s = t; s < a.num_parts; s += T) M = fmaxf(M, lp[(int64_t)s * a.pl_part]);
+    const int wspan = T < 64 ? T : 64;
+    for (int off = wspan / 2; off > 0; off >>= 1) M = fmaxf(M, xor_shfl(M, off));
+    if (T > 64) {
+        if (lane == 0) wmax[tid >> 6] = M;
+        __syncthreads();
+        const int w0 = rib * (T / 64);  // the waves of this row
+        M = wmax[w0];
+        for (int w = 1; w < T / 64; ++w) M = fmaxf(M, wmax[w0 + w]);
+    }
     const float Mu = M == -INFINITY ? 0.f : M;
 
-    // pass 2: weights and the weighted sum of this lane's slice
+    // 2. weighted sum over this part-group's parts
     float acc[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) acc[j] = 0.f;
     float W = 0.f;
-    int s = 0;
-    for (; s + 2 <= a.num_parts; s += 2) {
-        const float w0 = fast_exp2(lp[(int64_t)s * a.pl_part] - Mu);
-        const float w1 = fast_exp2(lp[(int64_t)(s + 1) * a.pl_part] - Mu);
-        float x0[VEC], x1[VEC];
-        PartLoad<TP>::load(op + (int64_t)s * a.po_part, x0);
-        PartLoad<TP>::load(op + (int64_t)(s + 1) * a.po_part, x1);
-        W += w0 + w1;
+    if (live) {
+        int s = pg;
+        for (; s + P < a.num_parts; s += 2 * P) {
+            const float l0 = lp[(int64_t)s * a.pl_part], l1 = lp[(int64_t)(s + P) * a.pl_part];
+            float x0[VEC], x1[VEC];
+            PartLoad<TP>::load(op + (int64_t)s * a.po_part, x0);
+            PartLoad<TP>::load(op + (int64_t)(s + P) * a.po_part, x1);
+            const float w0 = fast_exp2(l0 - Mu), w1 = fast_exp2(l1 - Mu);
+            W += w0 + w1;
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) acc[j] += w0 * x0[j] + w1 * x1[j];
-    }
-    if (s < a.num_parts) {
-        const float w0 = fast_exp2(lp[(int64_t)s * a.pl_part] - Mu);
-        float x0[VEC];
-        PartLoad<TP>::load(op + (int64_t)s * a.po_part, x0);
-        W += w0;
+            for (int j = 0; j < VEC; ++j) acc[j] += w0 * x0[j] + w1 * x1[j];
+        }
+        if (s < a.num_parts) {
+            const float l0 = lp[(int64_t)s * a.pl_part];
+            float x0[VEC];
+            PartLoad<TP>::load(op + (int64_t)s * a.po_part, x0);
+            const float w0 = fast_exp2(l0 - Mu);
+            W += w0;
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) acc[j] += w0 * x0[j];
+            for (int j = 0; j < VEC; ++j) acc[j] += w0 * x0[j];
+        }
     }
+
+    // 3. add the part-groups
+    if (P > 1) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) red[tid * (VEC + 1) + j] = acc[j];
+        red[tid * (VEC + 1) + VEC] = W;
+        __syncthreads();
+        if (pg != 0) return;
+        for (int g = 1; g < P; ++g) {
+            const float* o = &red[(tid + g * LPR) * (VEC + 1)];
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) acc[j] += o[j];
+            W += o[VEC];
+        }
+    }
+    if (!live) return;
     const float inv = W > 0.f ? 1.f / W : 0.f;
 #pragma unroll
     for (int j = 0; j < VEC; ++j) acc[j] *= inv;
@@ -132,10 +173,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 template <typename TP, typename TO, int D>
 hipError_t launch_merge_t(const MergeArgs& a, hipStream_t st) {
     constexpr int VEC = PartLoad<TP>::VEC;
-    constexpr int RPB = 4 * (64 / (D / VEC));  // rows per block
-    const int64_t blocks = (a.rows + RPB - 1) / RPB;
+    constexpr int LPR = D / VEC;
+    // part-groups: a power of two, about one part per group and lane, within 256 lanes
+    int P = 1;
+    while (P < a.num_parts && LPR * P * 2 <= 256) P *= 2;
+    const int rows_per_block = 256 / (LPR * P);
+    const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((merge_kernel<TP, TO, D>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((merge_kernel<TP, TO, D>), dim3((unsigned)blocks), dim3(256), 0, st, a, P);
     return hipGetLastError();
 }
 

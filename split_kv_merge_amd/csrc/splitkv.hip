@@ -13,7 +13,8 @@
 //
 // Per 32-key block and wave: S^T = K Q^T on two v_mfma_f32_16x16x32 tiles (keys on
 // M, query rows on N), K fed straight from global memory in the operand layout
-// (each lane loads D/4 contiguous elements of one key row); O^T += V^T P^T with
+// (k-step kk takes head-dim elements [32kk, 32kk + 32) of 16 key rows, the four
+// lanes of a row reading 64 contiguous bytes); O^T += V^T P^T with
 // V staged in a per-wave LDS slice and read back with ds_read_b64_tr_b16, the key
 // order of P matching the C layout of S^T.
 #include "device.h"
@@ -34,7 +35,102 @@ template <int D> struct SplitLds {
     static constexpr int BYTES = STAGE > COMB ? STAGE : COMB;
 };
 
+// Device-scope (agent) relaxed atomic accesses: on gfx950 these go through the
+// XCDs' L2 caches coherently (stores write through, loads bypass stale lines), so
+// data one work group publishes this way is visible to a work group on another
+// XCD without a whole-L2 write-back or invalidate (which a device-scope fence
+// would issue, once per work group).
+__device__ __forceinline__ void store_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Single-launch decode: once a work group has written its chunk's partial state
+// (with store_agent) it waits for those stores to complete and takes a ticket for
+// its (batch, kv head); the last of the num_splits work groups to arrive merges
+// all partial states of those rows the stable way -- global max M of the chunk
+// LSEs, weights 2^(lse_s - M) -- reading them with load_agent, writes the output
+// and its LSE, and returns the ticket counter to zero for the next call.
+// The merge keeps its memory latency off serial chains: all R x S partial LSEs
+// are fetched at once into LDS, and the output sum issues 8 part loads per wait.
+static_assert(16 * kMaxDecodeSplits + 32 <= SplitLds<64>::BYTES / 4, "merge weights fit in LDS");
+
 template <typename T, int D>
+__device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, int R, int G,
+                                           float* scratch) {
+    using E = Elem<T>;
+    __shared__ int is_last;
+    const int tid = threadIdx.x, S = a.num_splits;
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores are done
+    __syncthreads();                      // ... and every thread's
+    int* ticket = a.ticket + (int64_t)b * a.Hkv + hk;
+    if (tid == 0)
+        is_last = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  S - 1;
+    __syncthreads();
+    if (!is_last) return;
+
+    const int64_t lse_split = (int64_t)a.B * a.Hq * a.Lq;
+    float* wts = scratch;              // [R][S]: partial LSEs, then normalised weights
+    float* row_m = scratch + 16 * S;   // [R]: max
+    float* row_w = row_m + 16;         // [R]: sum of 2^(lse - max)
+    for (int idx = tid; idx < R * S; idx += 256) {
+        const int r = idx / S, sp = idx % S;
+        const int h = hk * G + r / a.Lq, i = r % a.Lq;
+        wts[idx] = load_agent(a.lse_part + sp * lse_split + ((int64_t)b * a.Hq + h) * a.Lq + i);
+    }
+    __syncthreads();
+    if (tid < R) {
+        float M = -INFINITY;
+        for (int sp = 0; sp < S; ++sp) M = fmaxf(M, wts[tid * S + sp]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float W = 0.f;
+        for (int sp = 0; sp < S; ++sp) W += fast_exp2(wts[tid * S + sp] - Mu);
+        const float inv = W > 0.f ? 1.f / W : 0.f;
+        for (int sp = 0; sp < S; ++sp) wts[tid * S + sp] = fast_exp2(wts[tid * S + sp] - Mu) * inv;
+        row_m[tid] = M;
+        row_w[tid] = W;
+    }
+    __syncthreads();
+
+    for (int it = tid; it < 16 * (D / 4); it += 256) {
+        const int r = it / (D / 4), d = (it % (D / 4)) * 4;
+        if (r >= R) break;
+        const int h = hk * G + r / a.Lq, i = r % a.Lq;
+        const int64_t row_off = (int64_t)b * a.q_batch + (int64_t)h * a.q_head + (int64_t)i * a.q_row;
+        const float* op = a.out_part + row_off + d;
+        const float* w = wts + r * S;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int sp0 = 0; sp0 < S; sp0 += 8) {
+            float x[8][4];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sp = min(sp0 + u, S - 1);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[u][c] = load_agent(op + sp * a.part_stride + c);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float wu = sp0 + u < S ? w[sp0 + u] : 0.f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[c] += wu * x[u][c];
+            }
+        }
+        u32x2 packed;
+        packed.x = E::pack2(acc[0], acc[1]);
+        packed.y = E::pack2(acc[2], acc[3]);
+        *reinterpret_cast<u32x2*>((uint16_t*)a.out + row_off + d) = packed;
+        if (d == 0 && a.lse) {
+            const float W = row_w[r];
+            a.lse[((int64_t)b * a.Hq + h) * a.Lq + i] = W > 0.f ? row_m[r] + fast_log2(W) : -INFINITY;
+        }
+    }
+    if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T, int D, bool FUSED>
 __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
     using E = Elem<T>;
     typedef SplitLds<D> L;
@@ -64,11 +160,11 @@ __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
     typename E::vec8 qf[NKK];
     {
         const uint16_t* qr = (const uint16_t*)a.q + (int64_t)b * a.q_batch +
-                             (int64_t)hq * a.q_head + (int64_t)iq * a.q_row + g4 * (D / 4);
+                             (int64_t)hq * a.q_head + (int64_t)iq * a.q_row + g4 * 8;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             u32x4 raw = {0u, 0u, 0u, 0u};
-            if (r_ok) raw = load16(qr + kk * 8);
+            if (r_ok) raw = load16(qr + kk * 32);
             qf[kk] = as_vec8<T>(raw);
         }
     }
@@ -76,27 +172,25 @@ __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
     const uint16_t* kp = (const uint16_t*)a.k + (int64_t)b * a.kv_batch + (int64_t)hk * a.kv_head;
     const uint16_t* vp = (const uint16_t*)a.v + (int64_t)b * a.kv_batch + (int64_t)hk * a.kv_head;
 
-    u32x4 kreg[2][NKK], vreg[VCH];
-    auto load_block = [&](int blk) {
+    // Loads of one block into a register buffer.  Rows past the chunk end are
+    // clamped to its last key (real, finite data; the chunk is non-empty whenever a
+    // block exists) and masked out of the softmax, so no load needs a branch.
+    typedef u32x4 KBuf[2][NKK];
+    typedef u32x4 VBuf[VCH];
+    auto load_block = [&](KBuf& kb_, VBuf& vb_, int blk) {
         const int kb = j0 + blk * kKeysPerBlock;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const int j = kb + hf * 16 + n;
-            const uint16_t* kr = kp + (int64_t)j * a.kv_row + g4 * (D / 4);
+            const int j = min(kb + hf * 16 + n, j1 - 1);
+            const uint16_t* kr = kp + (int64_t)j * a.kv_row + g4 * 8;
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                if (j < j1) z = load16(kr + kk * 8);
-                kreg[hf][kk] = z;
-            }
+            for (int kk = 0; kk < NKK; ++kk) kb_[hf][kk] = load16(kr + kk * 32);
         }
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = lane + 64 * u;
-            const int j = kb + c / CPR;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            if (j < j1) z = load16(vp + (int64_t)j * a.kv_row + (c % CPR) * 8);
-            vreg[u] = z;
+            const int j = min(kb + c / CPR, j1 - 1);
+            vb_[u] = load16(vp + (int64_t)j * a.kv_row + (c % CPR) * 8);
         }
     };
 
@@ -108,17 +202,7 @@ __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
     uint16_t* vl = (uint16_t*)smem + wave * kKeysPerBlock * VLD;
     const int e4 = (lane & 15) >> 2, q4 = lane & 3;
 
-    if (wave < nblk) load_block(wave);
-    for (int blk = wave; blk < nblk; blk += kWaves) {
-        u32x4 kc[2][NKK], vc[VCH];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) kc[hf][kk] = kreg[hf][kk];
-#pragma unroll
-        for (int u = 0; u < VCH; ++u) vc[u] = vreg[u];
-        if (blk + kWaves < nblk) load_block(blk + kWaves);
-
+    auto compute_block = [&](const KBuf& kc, const VBuf& vc, int blk) {
         // S^T for keys [16hf, 16hf + 16) of the block: lane holds keys 16hf + 4g4 + i.
         f32x4 sv[2];
 #pragma unroll
@@ -176,6 +260,23 @@ __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
             o[db] = E::mfma16(as_vec8<T>(av), as_vec8<T>(pb), o[db]);
         }
         lds_wave_sync();
+    };
+
+    // Ping-pong between two register buffers: the loads of the wave's next block
+    // are in flight while the current one is computed.  The prefetch is issued
+    // unconditionally (past the wave's last block it re-reads the current block,
+    // an L2 hit) and never copied between registers, so the compiler's wait counts
+    // only cover the older group of loads.
+    KBuf ka, kb2;
+    VBuf va, vb2;
+    if (wave < nblk) load_block(ka, va, wave);
+    for (int blk = wave; blk < nblk; blk += 2 * kWaves) {
+        const int nxt = blk + kWaves;
+        load_block(kb2, vb2, nxt < nblk ? nxt : blk);
+        compute_block(ka, va, blk);
+        if (nxt >= nblk) break;
+        load_block(ka, va, nxt + kWaves < nblk ? nxt + kWaves : nxt);
+        compute_block(kb2, vb2, nxt);
     }
 
     // The four lanes of a row hold disjoint keys: total their sums.
@@ -215,30 +316,45 @@ __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
         const int h = hk * G + r / a.Lq, i = r % a.Lq;
         float* op = a.out_part + (int64_t)s * a.part_stride + (int64_t)b * a.q_batch +
                     (int64_t)h * a.q_head + (int64_t)i * a.q_row + d;
-        *reinterpret_cast<f32x4*>(op) = acc * inv;
-        if (d == 0)
-            a.lse_part[(((int64_t)s * a.B + b) * a.Hq + h) * a.Lq + i] =
-                Ls > 0.f ? M + fast_log2(Ls) : -INFINITY;
+        float* lp = a.lse_part + (((int64_t)s * a.B + b) * a.Hq + h) * a.Lq + i;
+        const float lse_s = Ls > 0.f ? M + fast_log2(Ls) : -INFINITY;
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) store_agent(op + c, acc[c] * inv);
+            if (d == 0) store_agent(lp, lse_s);
+        } else {
+            *reinterpret_cast<f32x4*>(op) = acc * inv;
+            if (d == 0) *lp = lse_s;
+        }
     }
+    if constexpr (FUSED) merge_tail<T, D>(a, b, hk, R, G, (float*)smem);
+}
+
+template <typename T, int D>
+hipError_t launch_splitkv_f(const SplitArgs& a, bool fused, dim3 grid, hipStream_t st) {
+    if (fused)
+        hipLaunchKernelGGL((splitkv_kernel<T, D, true>), grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((splitkv_kernel<T, D, false>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_splitkv_t(const SplitArgs& a, int D, hipStream_t st) {
-    const dim3 grid((unsigned)a.num_splits, (unsigned)a.Hkv, (unsigned)a.B), block(256);
+hipError_t launch_splitkv_t(const SplitArgs& a, int D, bool fused, hipStream_t st) {
+    const dim3 grid((unsigned)a.num_splits, (unsigned)a.Hkv, (unsigned)a.B);
     switch (D) {
-        case 64: hipLaunchKernelGGL((splitkv_kernel<T, 64>), grid, block, 0, st, a); break;
-        case 128: hipLaunchKernelGGL((splitkv_kernel<T, 128>), grid, block, 0, st, a); break;
-        case 256: hipLaunchKernelGGL((splitkv_kernel<T, 256>), grid, block, 0, st, a); break;
+        case 64: return launch_splitkv_f<T, 64>(a, fused, grid, st);
+        case 128: return launch_splitkv_f<T, 128>(a, fused, grid, st);
+        case 256: return launch_splitkv_f<T, 256>(a, fused, grid, st);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_splitkv(const SplitArgs& a, int dtype, int D, hipStream_t stream) {
-    if (dtype == 0) return launch_splitkv_t<__bf16>(a, D, stream);
-    return launch_splitkv_t<_Float16>(a, D, stream);
+hipError_t launch_splitkv(const SplitArgs& a, int dtype, int D, bool fused, hipStream_t stream) {
+    if (dtype == 0) return launch_splitkv_t<__bf16>(a, D, fused, stream);
+    return launch_splitkv_t<_Float16>(a, D, fused, stream);
 }
 
 }  // namespace skv

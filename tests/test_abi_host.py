@@ -169,3 +169,24 @@ def test_lse_varlen_to_dense_checks_shape():
     assert dense[1, 0, 1] == lse[0, 3]
     with pytest.raises(ValueError):
         skv.lse_varlen_to_dense(lse, 4, 2)
+
+
+def test_splitkv_decode_rejects(lib):
+    P = FAKE
+    ws = ctypes.c_void_p(0x20000)   # 256-byte aligned
+
+    def call(**kw):
+        a = dict(B=2, Hq=32, Hkv=8, Lq=1, Lkv=4096, D=128, S=8, ws=ws, wsb=1 << 30, out=P)
+        a.update(kw)
+        return lib.skv_attn_splitkv_decode(P, P, P, a["out"], None, a["B"], a["Hq"], a["Hkv"],
+                                           a["Lq"], a["Lkv"], a["D"], 0, 0, 0.1, a["S"], a["ws"],
+                                           a["wsb"], None)
+    assert call(S=257) == 2          # the merge keeps S weights per row in LDS
+    assert call(ws=None) == 1
+    assert call(ws=ctypes.c_void_p(0x20010)) == 1     # not 256-byte aligned
+    assert call(wsb=16) == 1
+    assert call(out=None) == 1
+    assert call(B=0) == 0
+    need = lib.skv_splitkv_workspace_bytes(2, 32, 1, 128, 8, 8)
+    rows = 8 * 2 * 32
+    assert need == ((rows * 128 * 4 + 255) // 256 + (rows * 4 + 255) // 256 + 1) * 256

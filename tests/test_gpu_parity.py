@@ -206,3 +206,96 @@ def test_merge_fp16_parts_ring_style(skv):
     ro, rl = _oracle_attn(p, "fp16")
     assert_lse_close(lse.cpu(), rl)
     assert_out_close(out.cpu(), ro)
+
+
+# ------------------------------------------------------ merge_state alone
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 16, 33, 64, 100])
+@pytest.mark.parametrize("D,pdt", [(64, torch.float16), (128, torch.float32), (256, torch.float32),
+                                   (128, torch.bfloat16)])
+def test_merge_state_random_parts(skv, S, D, pdt):
+    """Random partial states, including parts with lse = -inf and a row whose parts
+    are all -inf, against the oracle's merge of the same (rounded) values."""
+    g = torch.Generator().manual_seed(S * 1000 + D)
+    R = (3, 5, 7)
+    o = torch.randn((S,) + R + (D,), generator=g).to(pdt)
+    lse = (torch.rand((S,) + R, generator=g) * 80 - 40).float()
+    lse[torch.rand((S,) + R, generator=g) < 0.2] = float("-inf")
+    lse[:, 1, 2, 3] = float("-inf")
+    ro, rl = oracle.merge(o.double().numpy(), lse.double().numpy())
+    out, ml = skv.merge_state(o.to(DEV), lse.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_lse_close(ml.cpu(), rl)
+    assert_out_close(out.cpu(), ro)
+    assert (out[1, 2, 3] == 0).all() and torch.isneginf(ml[1, 2, 3])
+
+
+def test_merge_state_strided_nhd_output(skv):
+    """Parts in HND row order merged straight into an NHD output (strides only)."""
+    S, B, H, L, D = 5, 2, 4, 9, 128
+    g = torch.Generator().manual_seed(7)
+    o = torch.randn(S, B, H, L, D, generator=g)
+    lse = torch.randn(S, B, H, L, generator=g) * 10
+    ro, rl = oracle.merge(o.double().numpy(), lse.double().numpy())
+    out_nhd = _poison((B, L, H, D), torch.bfloat16)
+    lse_out = _poison((B, H, L), torch.float32)
+    skv.merge_state(o.to(DEV), lse.to(DEV), out=out_nhd.transpose(1, 2), lse=lse_out)
+    torch.cuda.synchronize()
+    assert_out_close(out_nhd.transpose(1, 2).cpu(), ro)
+    assert_lse_close(lse_out.cpu(), rl)
+
+
+# ------------------------------------------------ single-launch decode
+
+@pytest.mark.parametrize("case", SPLIT_CASES)
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+def test_splitkv_decode_single_launch(skv, case, layout):
+    """Partials + in-kernel merge by the last work group; three calls share one
+    workspace (the arrival counters must come back to zero each time)."""
+    B, Hq, Hkv, Lq, Lkv, D, S = case
+    p = wl.attn_problem(B, Hq, Hkv, Lq, Lkv, D, seed=303, layout=layout)
+    ro, rl = _oracle_attn(p, "bf16")
+    q, k, v = _gpu(p.q), _gpu(p.k), _gpu(p.v)
+    ws = torch.zeros(skv.splitkv_workspace_bytes(B, Hq, Lq, D, S, Hkv), dtype=torch.uint8,
+                     device=DEV)
+    for _ in range(3):
+        out = _poison(q.shape, q.dtype)
+        lse = _poison((B, Hq, Lq), torch.float32)
+        skv.attn_splitkv_decode(q, k, v, num_splits=S, scale=p.scale, layout=layout, out=out,
+                                lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        assert_lse_close(lse.cpu(), rl)
+        assert_out_close(out.cpu(), ro)
+    # counters are back at zero
+    off = ws.numel() - ((B * Hkv * 4 + 255) // 256) * 256
+    assert (ws[off:off + B * Hkv * 4] == 0).all()
+
+
+def test_splitkv_decode_graph_replays(skv):
+    """Captured once, replayed with different inputs copied in between: every replay
+    matches the oracle (the workspace stays reusable across replays)."""
+    B, Hq, Hkv, Lq, Lkv, D, S = 2, 32, 8, 1, 3000, 128, 8
+    probs = [wl.attn_problem(B, Hq, Hkv, Lq, Lkv, D, seed=400 + i) for i in range(3)]
+    q = _gpu(probs[0].q); k = _gpu(probs[0].k); v = _gpu(probs[0].v)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(skv.splitkv_workspace_bytes(B, Hq, Lq, D, S, Hkv), dtype=torch.uint8,
+                     device=DEV)
+    fn = lambda: skv.attn_splitkv_decode(q, k, v, num_splits=S, scale=probs[0].scale, out=out,
+                                         lse=lse, workspace=ws)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        fn()
+    torch.cuda.current_stream().wait_stream(st)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for p in probs + probs[:1]:
+        q.copy_(p.q); k.copy_(p.k); v.copy_(p.v)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ro, rl = _oracle_attn(p, "bf16")
+        assert_lse_close(lse.cpu(), rl)
+        assert_out_close(out.cpu(), ro)
