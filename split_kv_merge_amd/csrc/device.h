@@ -15,6 +15,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -31,8 +34,9 @@ template <> struct Elem<__bf16> {
     static __device__ __forceinline__ uint16_t from_float(float f) {
         return __builtin_bit_cast(uint16_t, (__bf16)f);
     }
+    // two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
     static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-        return (uint32_t)from_float(a) | ((uint32_t)from_float(b) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
     }
     // 32x32x16: A [32 x 16], B [16 x 32], 8 elements per lane each
     static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
@@ -53,7 +57,7 @@ template <> struct Elem<_Float16> {
         return __builtin_bit_cast(uint16_t, (_Float16)f);
     }
     static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-        return (uint32_t)from_float(a) | ((uint32_t)from_float(b) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
     }
     static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);

@@ -30,16 +30,27 @@ namespace skv {
 
 namespace {
 
+template <bool B> struct BoolC {
+    static constexpr bool value = B;
+};
+
 template <int D> struct FmhaTile {
     static constexpr int BM = 128;                 // query rows per work group
     static constexpr int BN = D == 256 ? 32 : 64;  // keys per tile
     static constexpr int KLD = D + 8;              // K row pitch in LDS (elements)
-    static constexpr int VLD = D + 16;             // V row pitch in LDS (elements)
+    // V row pitch in LDS (elements): 16 dwords past a multiple of 64 banks, so each
+    // 32-lane pass of the transpose read (4 rows x 2 column groups x 4 lanes x 2
+    // dwords) touches all 64 banks once.
+    static constexpr int VLD = D + 32;
     static constexpr int NCH = BN * D / 8 / 256;   // 16-byte chunks per thread per tile
 };
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(256) void fmha_fwd_kernel(FmhaArgs a) {
+// LDS allows two work groups (two waves per SIMD) per compute unit; telling the
+// compiler so lets it spend up to 256 registers on keeping loads ahead of the MFMAs
+// instead of squeezing for an occupancy the LDS budget cannot reach.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
+void fmha_fwd_kernel(FmhaArgs a) {
     using E = Elem<T>;
     typedef typename E::vec8 V8;
     typedef FmhaTile<D> Tl;
@@ -49,8 +60,8 @@ __global__ __launch_bounds__(256) void fmha_fwd_kernel(FmhaArgs a) {
     constexpr int NDB = D / 32;   // 32-wide blocks of the output head dimension
     constexpr int CPR = D / 8;    // 16-byte chunks per K/V row
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * KLD];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[BN * VLD];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KLD];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN * VLD];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, hg = lane >> 5;
@@ -120,95 +131,90 @@ __global__ __launch_bounds__(256) void fmha_fwd_kernel(FmhaArgs a) {
     if (CAUSAL) kv_end = min(Lk, m0 + BM + Lk - Lq);
     const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     const int diag = Lk - Lq;  // row i sees keys j <= i + diag
+    // Tiles from this index on need a mask (the key tail, or the causal diagonal of
+    // the work group's first row); the ones before it are used whole.
+    int first_masked = Lk / BN;
+    if (CAUSAL) first_masked = min(first_masked, max(0, (m0 + diag + 1) / BN));
 
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    // Online softmax with a lazily moved reference max m_ref (log2 units, smoothed
+    // logits): it only moves when a tile's max exceeds it by more than kTau, so most
+    // tiles skip rescaling O and l.  Every p = 2^(s - m_ref) stays <= 2^kTau.
+    constexpr float kTau = 8.f;
+    float m_ref = -INFINITY, l_run = 0.f;
+    const float c = a.scale_log2;
 
-    // K/V tile loads.  Rows past the last key are clamped to it (real, finite data;
-    // a tile exists only when Lk > 0) and masked out of the softmax, so no load
-    // needs a branch.
-    u32x4 kr[NCH], vr[NCH];
-    auto load_tile = [&](int t) {
+    // K/V tile loads: chunk ci of this thread is key ch / CPR, column (ch % CPR) * 8,
+    // ch = tid + 256 ci; its offset inside a tile is a 32-bit constant and the tile
+    // base is uniform.  In masked tiles, rows past the last key are clamped to it
+    // (real, finite data; a tile exists only when Lk > 0) and masked out of the
+    // softmax, so no load needs a branch.
+    int koff[NCH];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int ch = tid + c * 256;
-            const int key = ch / CPR, col = (ch % CPR) * 8;
-            const int j = min(t * BN + key, Lk - 1);
-            kr[c] = load16(kp + (int64_t)j * a.kv_row + col);
-            vr[c] = load16(vp + (int64_t)j * a.kv_row + col);
+    for (int ci = 0; ci < NCH; ++ci) {
+        const int ch = tid + ci * 256;
+        koff[ci] = (ch / CPR) * (int)a.kv_row + (ch % CPR) * 8;
+    }
+    u32x4 kr[NCH], vr[NCH];
+    auto load_tile = [&](int t, bool clamp) {
+        const int64_t tb = (int64_t)t * BN * a.kv_row;
+        const uint16_t* kt = kp + tb;
+        const uint16_t* vt = vp + tb;
+#pragma unroll
+        for (int ci = 0; ci < NCH; ++ci) {
+            int off = koff[ci];
+            if (clamp) {
+                const int ch = tid + ci * 256;
+                const int key = min(ch / CPR, Lk - 1 - t * BN);
+                off = key * (int)a.kv_row + (ch % CPR) * 8;
+            }
+            kr[ci] = load16(kt + off);
+            vr[ci] = load16(vt + off);
         }
     };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int ci = 0; ci < NCH; ++ci) {
+            const int ch = tid + ci * 256;
+            const int key = ch / CPR, col = (ch % CPR) * 8;
+            store16(&k_lds[buf][key * KLD + col], kr[ci]);
+            store16(&v_lds[buf][key * VLD + col], vr[ci]);
+        }
+    };
+    const int full_tiles = Lk / BN;  // tiles with no key past the end
 
     // Lane roles for the transpose read of V^T operands.
     const int g16 = lane >> 4, e4 = (lane & 15) >> 2, q4 = lane & 3;
 
-    if (ntiles > 0) load_tile(0);
-    for (int t = 0; t < ntiles; ++t) {
-        __syncthreads();  // every wave is done with the previous tile
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int ch = tid + c * 256;
-            const int key = ch / CPR, col = (ch % CPR) * 8;
-            store16(&k_lds[key * KLD + col], kr[c]);
-            store16(&v_lds[key * VLD + col], vr[c]);
-        }
-        __syncthreads();
-        if (t + 1 < ntiles) load_tile(t + 1);
-
-        // S^T[key, row] for each 32-key block.
-        f32x16 s[NJB];
+    // One key tile: S^T = K Q^T, (mask,) online softmax, O^T += V^T P^T, then stage
+    // the next tile.  MASK is a compile-time switch so unmasked tiles carry no mask
+    // arithmetic.
+    auto process = [&](int t, auto mask_c) {
+        constexpr bool MASK = decltype(mask_c)::value;
+        const int buf = t & 1;
+        // Operands from LDS, issued ahead of their MFMAs: the 16-byte K rows of every
+        // k-step first, then the V^T transpose reads interleaved with the QK MFMAs,
+        // so their latency hides behind the QK product and the softmax.
+        u32x4 kop[NJB][NKK];
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-            s[jb] = f32x16{};
-            const uint16_t* kr0 = &k_lds[(jb * 32 + n) * KLD + hg * (D / 2)];
+            const uint16_t* kr0 = &k_lds[buf][(jb * 32 + n) * KLD + hg * (D / 2)];
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                s[jb] = E::mfma32(as_vec8<T>(load16(kr0 + kk * 8)), qf[kk], s[jb]);
+            for (int kk = 0; kk < NKK; ++kk) kop[jb][kk] = load16(kr0 + kk * 8);
         }
-
-        // scale, mask, running max (lane holds keys 8(i/4) + 4hg + i%4 of each block)
-        const int kbase = t * BN;
-        float mx = -INFINITY;
+        f32x16 s[NJB];
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb)
+        for (int jb = 0; jb < NJB; ++jb) s[jb] = f32x16{};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = kbase + jb * 32 + 8 * (i >> 2) + hg * 4 + (i & 3);
-                float x = s[jb][i] * a.scale_log2 - bias;
-                bool ok = key < Lk;
-                if (CAUSAL) ok = ok && key <= row + diag;
-                x = ok ? x : -INFINITY;
-                s[jb][i] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = fmaxf(mx, xor_shfl(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
-
-        // p = 2^(s - m), packed to 16-bit as the B operand of the PV product
-        uint32_t pk[NJB][2][4];
-        float psum = 0.f;
+        for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float p0 = fast_exp2(s[jb][8 * st + 2 * j] - m_use);
-                    const float p1 = fast_exp2(s[jb][8 * st + 2 * j + 1] - m_use);
-                    psum += p0 + p1;
-                    pk[jb][st][j] = E::pack2(p0, p1);
-                }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-
-        // O^T[d, row] += V^T[d, keys] P^T[keys, row]; k-step st of block jb covers
-        // keys 16st + 8h + 4(lane/32) + e for operand slots 4h + e.
+            for (int jb = 0; jb < NJB; ++jb)
+                s[jb] = E::mfma32(as_vec8<T>(kop[jb][kk]), qf[kk], s[jb]);
+        // V^T operands: k-step st of block jb covers keys 16st + 8h + 4(lane/32) + e
+        // for operand slots 4h + e (the order the C layout of S^T leaves P in).
+        u32x4 vop[NDB][NJB][2];
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -217,16 +223,95 @@ __global__ __launch_bounds__(256) void fmha_fwd_kernel(FmhaArgs a) {
                 for (int st = 0; st < 2; ++st) {
                     const int key0 = jb * 32 + 16 * st + 4 * (g16 >> 1) + e4;
                     const int col = db * 32 + (g16 & 1) * 16 + 4 * q4;
-                    const u32x2 lo = lds_read_tr16(&v_lds[key0 * VLD + col]);
-                    const u32x2 hi = lds_read_tr16(&v_lds[(key0 + 8) * VLD + col]);
-                    const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
+                    const u32x2 lo = lds_read_tr16(&v_lds[buf][key0 * VLD + col]);
+                    const u32x2 hi = lds_read_tr16(&v_lds[buf][(key0 + 8) * VLD + col]);
+                    vop[db][jb][st] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                }
+        __builtin_amdgcn_sched_group_barrier(0x100, NJB * NKK, 0);  // K reads
+#pragma unroll
+        for (int i = 0; i < NJB * NKK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one QK MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDB * NJB * 2 / (NJB * NKK), 0);
+        }
+        if constexpr (MASK) {
+            // lane holds keys 8(i/4) + 4hg + i%4 of each 32-key block
+            const int kbase = t * BN;
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kbase + jb * 32 + 8 * (i >> 2) + hg * 4 + (i & 3);
+                    bool ok = key < Lk;
+                    if (CAUSAL) ok = ok && key <= row + diag;
+                    s[jb][i] = ok ? s[jb][i] : -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[jb][i]);
+        mx = fmaxf(mx, xor_shfl(mx, 32));
+        const float m_tile = mx == -INFINITY ? -INFINITY : mx * c - bias;
+        if (__any(m_tile > m_ref + kTau)) {
+            const float m_new = m_tile > m_ref + kTau ? m_tile : m_ref;
+            const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
+            m_ref = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        }
+        const float nb = -(bias + (m_ref == -INFINITY ? 0.f : m_ref));
+
+        // p = 2^(s*c - bias - m_ref), packed to 16-bit as the B operand of PV
+        uint32_t pk[NJB][2][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float p0 = fast_exp2(fmaf(s[jb][8 * st + 2 * j], c, nb));
+                    const float p1 = fast_exp2(fmaf(s[jb][8 * st + 2 * j + 1], c, nb));
+                    psum += p0 + p1;
+                    pk[jb][st][j] = E::pack2(p0, p1);
+                }
+        l_run += psum;
+
+        // O^T[d, row] += V^T[d, keys] P^T[keys, row]
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
                     const u32x4 bv = {pk[jb][st][0], pk[jb][st][1], pk[jb][st][2],
                                       pk[jb][st][3]};
-                    o[db] = E::mfma32(as_vec8<T>(av), as_vec8<T>(bv), o[db]);
+                    o[db] = E::mfma32(as_vec8<T>(vop[db][jb][st]), as_vec8<T>(bv), o[db]);
                 }
-    }
 
-    // Epilogue: out = O / l; LSE = m + log2(l) (+ smoothing bias), one store per row.
+        if (t + 1 < ntiles) {
+            store_tile(buf ^ 1);
+            if (t + 2 < ntiles) load_tile(t + 2, t + 2 >= full_tiles);
+        }
+        __syncthreads();
+    };
+
+    // Two LDS buffers: tile t is computed from buffer t&1 while tile t+1 is stored
+    // into the other one and tile t+2 is being loaded; one barrier per tile.
+    if (ntiles > 0) {
+        load_tile(0, 0 >= full_tiles);
+        store_tile(0);
+        if (ntiles > 1) load_tile(1, 1 >= full_tiles);
+    }
+    __syncthreads();
+    const int nfree = min(first_masked, ntiles);
+    int t = 0;
+    for (; t < nfree; ++t) process(t, BoolC<false>{});
+    for (; t < ntiles; ++t) process(t, BoolC<true>{});
+
+    // Epilogue: out = O / l; LSE = m_ref + log2(l) (+ smoothing bias), one store per row.
     const float l_tot = l_run + xor_shfl(l_run, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (row_ok) {
@@ -243,7 +328,7 @@ __global__ __launch_bounds__(256) void fmha_fwd_kernel(FmhaArgs a) {
             }
         if (hg == 0 && a.lse)
             a.lse[lse_off + (int64_t)h * a.lse_head + row] =
-                l_tot > 0.f ? m_run + fast_log2(l_tot) + bias : -INFINITY;
+                l_tot > 0.f ? m_ref + fast_log2(l_tot) + bias : -INFINITY;
     }
 }
 
