@@ -358,6 +358,31 @@ def secondary(skv, args):
     return res
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_gqa_splitkv_decode_hbm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "split_kv_merge_amd", "csrc", f)
+                  for f in ("splitkv.hip", "device.h", "launch.h")]
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter record, or
+    None when the record is missing or the kernel source changed since it was taken."""
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def copy_probe():
     """A plain device copy of known size (256 MiB read + 256 MiB written), for
     scaling the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
@@ -412,7 +437,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "kernel": "splitkv_kernel<bf16, 128, single-launch> (skv_attn_splitkv_decode)",
             "avg_launch_us": round(h["avg_us"], 2),
             "algorithmic_bytes_per_launch": int(h["avg_bytes"]),

@@ -1,0 +1,73 @@
+"""Run the micro-benchmarks of ceilings.hip and print one line per ceiling.
+
+    python microbench/ceilings.py        (needs microbench/libceilings.so, built by
+                                          __graft_entry__.build())
+Rates per compute unit assume the 2.4 GHz peak clock.
+"""
+import ctypes
+import os
+import sys
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "libceilings.so")
+
+
+def build():
+    import subprocess
+    subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-shared", "-fPIC",
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                    "-o", LIB, os.path.join(HERE, "ceilings.hip")], check=True,
+                   capture_output=True)
+    return LIB
+
+
+def measure():
+    lib = ctypes.CDLL(LIB)
+    lib.run.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                        ctypes.c_int, ctypes.c_void_p]
+    out = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def t(which, grid, iters, p=None, n=0, reps=5):
+        for _ in range(2):
+            assert lib.run(which, p, n, ctypes.c_void_p(out.data_ptr()), grid, iters, st) == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            lib.run(which, p, n, ctypes.c_void_p(out.data_ptr()), grid, iters, st)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    CU, CLK = 256, 2.4e9
+    res = {}
+    g, it = CU * 4, 2000
+    sec = t(0, g, it)
+    res["lds_read_b128_B_per_clk_per_cu"] = g * 256 * 16 * 16 * it / sec / CU / CLK
+    sec = t(1, g, it)
+    res["lds_read_tr16_b64_B_per_clk_per_cu"] = g * 256 * 8 * 16 * it / sec / CU / CLK
+    g2 = CU * 2
+    sec = t(2, g2, 2000)
+    res["mfma_bf16_32x32x16_tflops"] = g2 * 4 * 4 * 32768 * 2000 / sec / 1e12
+    g2 = CU * 4
+    sec = t(3, g2, 2000)
+    res["exp_f32_lanes_per_clk_per_cu"] = g2 * 256 * 8 * 2000 / sec / CU / CLK
+    sec = t(4, g2, 2000)
+    res["fma_f32_lanes_per_clk_per_cu"] = g2 * 256 * 8 * 2000 / sec / CU / CLK
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    best = 0.0
+    for grid in (2048, 4096, 8192):
+        sec = t(5, grid, 0, ctypes.c_void_p(buf.data_ptr()), buf.numel() // 16)
+        best = max(best, buf.numel() / sec / 1e9)
+    res["hbm_read_stream_GBs"] = best
+    return res
+
+
+if __name__ == "__main__":
+    if not os.path.exists(LIB):
+        sys.exit("microbench/libceilings.so is not built")
+    for k, v in measure().items():
+        print(f"{k}: {v:.1f}", flush=True)
