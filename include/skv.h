@@ -141,7 +141,8 @@ skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* 
  * a separate serial path].
  *
  *   q, k, v, layout, num_splits: as skv_attn_splitkv_partial; num_splits <= 256
- *       (SKV_EUNSUPPORTED beyond).
+ *       and num_splits*B*Hq*Lq*D*4 < 2^31 bytes of partial states (SKV_EUNSUPPORTED
+ *       beyond).
  *   out  q's shape, layout and dtype: the merged output.
  *   lse  float32 [B, Hq, Lq] (log2) or NULL.
  *   workspace: device memory of skv_splitkv_workspace_bytes(B, Hq, Lq, D,

@@ -314,6 +314,8 @@ skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v
         return fail(SKV_EINVAL, "workspace has %zu bytes, the decode needs %zu", workspace_bytes, need);
     if (B == 0) return SKV_OK;
     const size_t rows = (size_t)num_splits * B * Hq * Lq;
+    if (rows * D * sizeof(float) >= ((size_t)1 << 31))
+        return fail(SKV_EUNSUPPORTED, "partial states exceed 2 GiB for the single-launch decode");
     char* ws = (char*)workspace;
     a.out_part = (float*)ws;
     a.lse_part = (float*)(ws + align256(rows * D * sizeof(float)));

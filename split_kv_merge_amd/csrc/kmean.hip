@@ -33,8 +33,23 @@ __global__ __launch_bounds__(256) void kmean_kernel(KmeanArgs a) {
     }
     const uint16_t* kp = (const uint16_t*)a.k + off + (int64_t)g * a.kv_head + (tid % CPR) * 8;
 
+    // Eight rows in flight per thread: the loop is latency-bound otherwise.
+    constexpr int U = 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = tid / CPR; j < Lk; j += RPP) {
+    int j = tid / CPR;
+    for (; j + (U - 1) * RPP < Lk; j += U * RPP) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = load16(kp + (int64_t)(j + u * RPP) * a.kv_row);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                acc[2 * w] += E::to_float((uint16_t)(v[u][w] & 0xffff));
+                acc[2 * w + 1] += E::to_float((uint16_t)(v[u][w] >> 16));
+            }
+    }
+    for (; j < Lk; j += RPP) {
         const u32x4 v = load16(kp + (int64_t)j * a.kv_row);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {

@@ -125,6 +125,21 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int P) {
     float W = 0.f;
     if (live) {
         int s = pg;
+        for (; s + 3 * P < a.num_parts; s += 4 * P) {  // four parts in flight
+            float x[4][VEC], l[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                l[u] = lp[(int64_t)(s + u * P) * a.pl_part];
+                PartLoad<TP>::load(op + (int64_t)(s + u * P) * a.po_part, x[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float w = fast_exp2(l[u] - Mu);
+                W += w;
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) acc[j] += w * x[u][j];
+            }
+        }
         for (; s + P < a.num_parts; s += 2 * P) {
             const float l0 = lp[(int64_t)s * a.pl_part], l1 = lp[(int64_t)(s + P) * a.pl_part];
             float x0[VEC], x1[VEC];
@@ -174,9 +189,12 @@ template <typename TP, typename TO, int D>
 hipError_t launch_merge_t(const MergeArgs& a, hipStream_t st) {
     constexpr int VEC = PartLoad<TP>::VEC;
     constexpr int LPR = D / VEC;
-    // part-groups: a power of two, about one part per group and lane, within 256 lanes
+    // Part-groups spread one row's parts over more lanes only when there are too few
+    // rows to fill the chip (fewer than ~4 x 256 CUs worth of 256-thread blocks with
+    // one lane group per row); then a power of two up to one part per group.
     int P = 1;
-    while (P < a.num_parts && LPR * P * 2 <= 256) P *= 2;
+    if (a.rows * LPR < (int64_t)4 * 256 * 256)
+        while (P < a.num_parts && LPR * P * 2 <= 256) P *= 2;
     const int rows_per_block = 256 / (LPR * P);
     const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;

@@ -35,23 +35,23 @@ template <int D> struct SplitLds {
     static constexpr int BYTES = STAGE > COMB ? STAGE : COMB;
 };
 
-// Device-scope (agent) relaxed atomic accesses: on gfx950 these go through the
-// XCDs' L2 caches coherently (stores write through, loads bypass stale lines), so
-// data one work group publishes this way is visible to a work group on another
-// XCD without a whole-L2 write-back or invalidate (which a device-scope fence
-// would issue, once per work group).
+// Buffer resource word 3 for raw (untyped) buffer access on gfx950, and the
+// cache-policy bit that makes a buffer load device-coherent (sc1).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCoherentLoad = 0x10;
+
+// Device-scope (agent) relaxed atomic stores write through the XCD's L2, so data
+// one work group publishes this way reaches memory without the whole-L2 write-back
+// a device-scope release fence would issue (once per work group).
 __device__ __forceinline__ void store_agent(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Single-launch decode: once a work group has written its chunk's partial state
 // (with store_agent) it waits for those stores to complete and takes a ticket for
 // its (batch, kv head); the last of the num_splits work groups to arrive merges
 // all partial states of those rows the stable way -- global max M of the chunk
-// LSEs, weights 2^(lse_s - M) -- reading them with load_agent, writes the output
+// LSEs, weights 2^(lse_s - M) -- after a device-scope acquire, writes the output
 // and its LSE, and returns the ticket counter to zero for the next call.
 // The merge keeps its memory latency off serial chains: all R x S partial LSEs
 // are fetched at once into LDS, and the output sum issues 8 part loads per wait.
@@ -71,6 +71,13 @@ __device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, in
                   S - 1;
     __syncthreads();
     if (!is_last) return;
+    // The partials are read with device-coherent (sc1) buffer loads, which miss any
+    // stale line this XCD's L2 may hold, so no cache-wide invalidate is needed.
+    // Byte offsets stay below 2^31 (checked on the host).
+    const __amdgpu_buffer_rsrc_t po_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(a.out_part, (short)0, 0x7fffffff, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t pl_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(a.lse_part, (short)0, 0x7fffffff, kBufferRsrcWord3);
 
     const int64_t lse_split = (int64_t)a.B * a.Hq * a.Lq;
     float* wts = scratch;              // [R][S]: partial LSEs, then normalised weights
@@ -79,7 +86,9 @@ __device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, in
     for (int idx = tid; idx < R * S; idx += 256) {
         const int r = idx / S, sp = idx % S;
         const int h = hk * G + r / a.Lq, i = r % a.Lq;
-        wts[idx] = load_agent(a.lse_part + sp * lse_split + ((int64_t)b * a.Hq + h) * a.Lq + i);
+        const int64_t e = sp * lse_split + ((int64_t)b * a.Hq + h) * a.Lq + i;
+        wts[idx] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(pl_rsrc, (int)(e * 4), 0, kCoherentLoad));
     }
     __syncthreads();
     if (tid < R) {
@@ -100,23 +109,19 @@ __device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, in
         if (r >= R) break;
         const int h = hk * G + r / a.Lq, i = r % a.Lq;
         const int64_t row_off = (int64_t)b * a.q_batch + (int64_t)h * a.q_head + (int64_t)i * a.q_row;
-        const float* op = a.out_part + row_off + d;
+        const int64_t op = row_off + d;  // element offset of split 0
         const float* w = wts + r * S;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int sp0 = 0; sp0 < S; sp0 += 8) {
-            float x[8][4];
+            f32x4 x[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int sp = min(sp0 + u, S - 1);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) x[u][c] = load_agent(op + sp * a.part_stride + c);
+                const int64_t e = op + min(sp0 + u, S - 1) * a.part_stride;
+                x[u] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(po_rsrc, (int)(e * 4), 0, kCoherentLoad));
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float wu = sp0 + u < S ? w[sp0 + u] : 0.f;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[c] += wu * x[u][c];
-            }
+            for (int u = 0; u < 8; ++u) acc += x[u] * (sp0 + u < S ? w[sp0 + u] : 0.f);
         }
         u32x2 packed;
         packed.x = E::pack2(acc[0], acc[1]);
