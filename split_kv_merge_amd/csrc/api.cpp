@@ -156,7 +156,7 @@ skv_status_t skv_attn_fwd(const void* q, const void* k, const void* v, void* out
         if (st != SKV_OK) return st;
         a.kbar = (const float*)workspace;
     }
-    const int bm = skv::fmha_rows_per_block();
+    const int bm = skv::fmha_rows_per_block(D);
     const int grid_m = (int)(((int64_t)Sq + bm - 1) / bm);
     return launched(skv::launch_fmha(a, dtype, D, causal != 0, false, grid_m, B, s), "fmha_fwd");
 }
@@ -214,7 +214,7 @@ skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
         if (st != SKV_OK) return st;
         a.kbar = (const float*)workspace;
     }
-    const int bm = skv::fmha_rows_per_block();
+    const int bm = skv::fmha_rows_per_block(D);
     const int grid_m = (max_seqlen_q + bm - 1) / bm;
     return launched(skv::launch_fmha(a, dtype, D, causal != 0, true, grid_m, nseq, s), "fmha_fwd_varlen");
 }

@@ -8,7 +8,10 @@
 // (same report, second issue; Reproduction Steps part 3).
 //
 // Design (gfx950, wave64):
-//   * work group = 4 waves = 128 query rows; wave w owns rows [32w, 32w + 32).
+//   * work group = 8 waves = 256 query rows (4 waves = 128 rows for D = 256);
+//     wave w owns rows [32w, 32w + 32).  All waves of a compute unit share one
+//     staged K/V tile, so each tile is loaded and written to LDS once per 256
+//     rows rather than once per 128.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 with keys on the M axis and query rows on
 //     the N (lane) axis, so every lane owns exactly one query row: its running
 //     max and sum live in that lane (plus its partner lane^32), and the LSE
@@ -35,21 +38,25 @@ template <bool B> struct BoolC {
 };
 
 template <int D> struct FmhaTile {
-    static constexpr int BM = 128;                 // query rows per work group
+    // Waves per work group: two per SIMD.  At D = 256 a wave needs the whole
+    // 512-register file, so only one fits per SIMD.
+    static constexpr int NW = D == 256 ? 4 : 8;
+    static constexpr int NT = 64 * NW;             // threads per work group
+    static constexpr int BM = 32 * NW;             // query rows per work group
     static constexpr int BN = D == 256 ? 32 : 64;  // keys per tile
     static constexpr int KLD = D + 8;              // K row pitch in LDS (elements)
     // V row pitch in LDS (elements): 16 dwords past a multiple of 64 banks, so each
     // 32-lane pass of the transpose read (4 rows x 2 column groups x 4 lanes x 2
     // dwords) touches all 64 banks once.
     static constexpr int VLD = D + 32;
-    static constexpr int NCH = BN * D / 8 / 256;   // 16-byte chunks per thread per tile
+    static constexpr int NCH = BN * D / 8 / NT;    // 16-byte chunks per thread per tile
 };
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-// LDS allows two work groups (two waves per SIMD) per compute unit; telling the
-// compiler so lets it spend up to 256 registers on keeping loads ahead of the MFMAs
-// instead of squeezing for an occupancy the LDS budget cannot reach.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
+// One work group per compute unit (two waves per SIMD, one at D = 256); telling the
+// compiler so lets it spend up to 256 (512) registers on keeping loads ahead of the
+// MFMAs instead of squeezing for an occupancy the work-group size cannot reach.
+__global__ __launch_bounds__(FmhaTile<D>::NT) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
 void fmha_fwd_kernel(FmhaArgs a) {
     using E = Elem<T>;
     typedef typename E::vec8 V8;
@@ -147,14 +154,14 @@ void fmha_fwd_kernel(FmhaArgs a) {
     const float c = a.scale_log2;
 
     // K/V tile loads: chunk ci of this thread is key ch / CPR, column (ch % CPR) * 8,
-    // ch = tid + 256 ci; its offset inside a tile is a 32-bit constant and the tile
+    // ch = tid + NT ci; its offset inside a tile is a 32-bit constant and the tile
     // base is uniform.  In masked tiles, rows past the last key are clamped to it
     // (real, finite data; a tile exists only when Lk > 0) and masked out of the
     // softmax, so no load needs a branch.
     int koff[NCH];
 #pragma unroll
     for (int ci = 0; ci < NCH; ++ci) {
-        const int ch = tid + ci * 256;
+        const int ch = tid + ci * Tl::NT;
         koff[ci] = (ch / CPR) * (int)a.kv_row + (ch % CPR) * 8;
     }
     u32x4 kr[NCH], vr[NCH];
@@ -166,7 +173,7 @@ void fmha_fwd_kernel(FmhaArgs a) {
         for (int ci = 0; ci < NCH; ++ci) {
             int off = koff[ci];
             if (clamp) {
-                const int ch = tid + ci * 256;
+                const int ch = tid + ci * Tl::NT;
                 const int key = min(ch / CPR, Lk - 1 - t * BN);
                 off = key * (int)a.kv_row + (ch % CPR) * 8;
             }
@@ -177,7 +184,7 @@ void fmha_fwd_kernel(FmhaArgs a) {
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int ci = 0; ci < NCH; ++ci) {
-            const int ch = tid + ci * 256;
+            const int ch = tid + ci * Tl::NT;
             const int key = ch / CPR, col = (ch % CPR) * 8;
             store16(&k_lds[buf][key * KLD + col], kr[ci]);
             store16(&v_lds[buf][key * VLD + col], vr[ci]);
@@ -334,7 +341,7 @@ void fmha_fwd_kernel(FmhaArgs a) {
 
 template <typename T, int D>
 hipError_t launch_fmha_t(const FmhaArgs& a, bool causal, bool varlen, dim3 grid, hipStream_t st) {
-    const dim3 block(256);
+    const dim3 block(FmhaTile<D>::NT);
     if (causal) {
         if (varlen)
             hipLaunchKernelGGL((fmha_fwd_kernel<T, D, true, true>), grid, block, 0, st, a);
@@ -362,7 +369,13 @@ hipError_t launch_fmha_d(const FmhaArgs& a, int D, bool causal, bool varlen, dim
 
 }  // namespace
 
-int fmha_rows_per_block() { return FmhaTile<128>::BM; }
+int fmha_rows_per_block(int D) {
+    switch (D) {
+        case 64: return FmhaTile<64>::BM;
+        case 128: return FmhaTile<128>::BM;
+        default: return FmhaTile<256>::BM;
+    }
+}
 
 hipError_t launch_fmha(const FmhaArgs& a, int dtype, int D, bool causal, bool varlen, int grid_m,
                        int grid_b, hipStream_t stream) {

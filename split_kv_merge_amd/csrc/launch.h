@@ -67,7 +67,7 @@ struct MergeArgs {
     int64_t l_s0, l_s1, l_s2;
 };
 
-int fmha_rows_per_block();
+int fmha_rows_per_block(int D);  // query rows one attention work group covers
 hipError_t launch_fmha(const FmhaArgs& a, int dtype, int D, bool causal, bool varlen,
                        int grid_m, int grid_b, hipStream_t stream);
 hipError_t launch_kmean(const KmeanArgs& a, int dtype, int D, bool varlen, int grid_b,

@@ -86,6 +86,9 @@ DENSE_CASES = [
     (1, 2, 2, 64, 190, 256, True),
     (3, 6, 3, 1, 500, 128, False),
     (1, 4, 2, 300, 100, 64, True),    # Sq > Sk: early rows see no key (bottom-right)
+    (1, 4, 2, 777, 900, 128, True),   # four 256-row tiles, ragged last one
+    (2, 2, 1, 600, 513, 64, False),
+    (1, 2, 2, 530, 530, 256, True),   # five 128-row tiles at D = 256
 ]
 
 
