@@ -80,7 +80,9 @@ typedef enum { SKV_HND = 0, SKV_NHD = 1 } skv_layout_t;
  * initialisation required); without smoothing `workspace` may be NULL.
  *
  * Sizes: B, Sq, Sk >= 0 (zero-sized problems return SKV_OK without launching,
- * except Sk == 0 with Sq > 0, which writes zero outputs and -inf LSEs).
+ * except Sk == 0 with Sq > 0, which writes zero outputs and -inf LSEs).  Grid
+ * limits: B <= 65535 and at most 65535 row tiles (Sq <= 65535 * 256 at D <= 128,
+ * 65535 * 128 at D = 256); SKV_EUNSUPPORTED beyond.
  */
 skv_status_t skv_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                           int B, int Hq, int Hkv, int Sq, int Sk, int D, skv_dtype_t dtype,
@@ -100,7 +102,8 @@ skv_status_t skv_attn_fwd(const void* q, const void* k, const void* v, void* out
  *   lse: float32 [Hq, total_q] (2-D: head-major, token index as in q) or NULL.
  *
  * causal and smooth_k act per sequence as in skv_attn_fwd (mean(k) per sequence
- * and kv head; workspace of skv_workspace_bytes(nseq, Hkv, D, 1) bytes).
+ * and kv head; workspace of skv_workspace_bytes(nseq, Hkv, D, 1) bytes).  Grid
+ * limits as in skv_attn_fwd, with nseq for B and max_seqlen_q for Sq.
  */
 skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
                                  float* lse, const int32_t* cu_seqlens_q,

@@ -158,6 +158,8 @@ skv_status_t skv_attn_fwd(const void* q, const void* k, const void* v, void* out
     }
     const int bm = skv::fmha_rows_per_block(D);
     const int grid_m = (int)(((int64_t)Sq + bm - 1) / bm);
+    if (grid_m > 65535)
+        return fail(SKV_EUNSUPPORTED, "Sq=%d needs %d row tiles, over the 65535 grid limit", Sq, grid_m);
     return launched(skv::launch_fmha(a, dtype, D, causal != 0, false, grid_m, B, s), "fmha_fwd");
 }
 
@@ -216,6 +218,9 @@ skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
     }
     const int bm = skv::fmha_rows_per_block(D);
     const int grid_m = (max_seqlen_q + bm - 1) / bm;
+    if (grid_m > 65535)
+        return fail(SKV_EUNSUPPORTED, "max_seqlen_q=%d needs %d row tiles, over the 65535 grid limit",
+                    max_seqlen_q, grid_m);
     return launched(skv::launch_fmha(a, dtype, D, causal != 0, true, grid_m, nseq, s), "fmha_fwd_varlen");
 }
 

@@ -72,9 +72,15 @@ void fmha_fwd_kernel(FmhaArgs a) {
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, hg = lane >> 5;
-    const int b = blockIdx.z, h = blockIdx.y;
-    // causal: the longest (last) row tiles first, so they do not trail the grid
-    const int mt = CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+    // Grid (head, batch | sequence, row tile), dispatched head-fastest: with causal
+    // masking the row tiles run last-first, so the work groups go out in order of
+    // decreasing work (a row tile's key count grows with its index) across every
+    // head and sequence, and none of the long ones trails the grid.  Head-fastest
+    // also keeps each head's work groups on one XCD (work groups are dealt to the
+    // XCDs round-robin and Hq is normally a multiple of their count), so its K/V
+    // stays in one L2.
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int mt = CAUSAL ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
 
     int Lq, Lk;
     int64_t q_off, kv_off, lse_off;
@@ -379,7 +385,7 @@ int fmha_rows_per_block(int D) {
 
 hipError_t launch_fmha(const FmhaArgs& a, int dtype, int D, bool causal, bool varlen, int grid_m,
                        int grid_b, hipStream_t stream) {
-    const dim3 grid((unsigned)grid_m, (unsigned)a.Hq, (unsigned)grid_b);
+    const dim3 grid((unsigned)a.Hq, (unsigned)grid_b, (unsigned)grid_m);
     if (dtype == 0) return launch_fmha_d<__bf16>(a, D, causal, varlen, grid, stream);
     return launch_fmha_d<_Float16>(a, D, causal, varlen, grid, stream);
 }
