@@ -9,7 +9,7 @@
 //
 // Design (gfx950, wave64):
 //   * work group = 8 waves = 256 query rows (4 waves = 128 rows for D = 256);
-//     wave w owns rows [32w, 32w + 32).  All waves of a compute unit share one
+//     each wave owns one block of 32 rows.  All waves of a compute unit share one
 //     staged K/V tile, so each tile is loaded and written to LDS once per 256
 //     rows rather than once per 128.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 with keys on the M axis and query rows on
@@ -106,7 +106,11 @@ void fmha_fwd_kernel(FmhaArgs a) {
     const uint16_t* kp = (const uint16_t*)a.k + kv_off + (int64_t)g * a.kv_head;
     const uint16_t* vp = (const uint16_t*)a.v + kv_off + (int64_t)g * a.kv_head;
 
-    const int row = m0 + wave * 32 + n;
+    // Row block of this wave.  The two waves sharing a SIMD (w and w + 4) take
+    // mirrored blocks (w and 7 - w), so in the causal diagonal band, where later
+    // blocks see more keys, every SIMD carries about the same work.
+    const int rblk = (Tl::NW == 8 && wave >= 4) ? 11 - wave : wave;
+    const int row = m0 + rblk * 32 + n;
     const bool row_ok = row < Lq;
 
     // Q as the B operand: this lane holds q[row][hg*D/2 + 8kk .. +8) for each k-step.
@@ -148,6 +152,16 @@ void fmha_fwd_kernel(FmhaArgs a) {
     // the work group's first row); the ones before it are used whole.
     int first_masked = Lk / BN;
     if (CAUSAL) first_masked = min(first_masked, max(0, (m0 + diag + 1) / BN));
+    // Masked tiles this wave computes.  A tile entirely past the causal diagonal of
+    // the wave's last row, or any tile of a wave whose rows all lie past Lq, would
+    // only add masked (-inf) logits -- exactly nothing -- so the wave skips its math
+    // there (it still stages tiles and joins every barrier).
+    const int wrow0 = m0 + rblk * 32;
+    int wave_tiles = ntiles;
+    if (wrow0 >= Lq)
+        wave_tiles = 0;
+    else if (CAUSAL)
+        wave_tiles = min(ntiles, max(0, (min(wrow0 + 31, Lq - 1) + diag + BN) / BN));
 
     f32x16 o[NDB];
 #pragma unroll
@@ -207,103 +221,105 @@ void fmha_fwd_kernel(FmhaArgs a) {
     auto process = [&](int t, auto mask_c) {
         constexpr bool MASK = decltype(mask_c)::value;
         const int buf = t & 1;
-        // Operands from LDS, issued ahead of their MFMAs: the 16-byte K rows of every
-        // k-step first, then the V^T transpose reads interleaved with the QK MFMAs,
-        // so their latency hides behind the QK product and the softmax.
-        u32x4 kop[NJB][NKK];
+        // (unmasked tiles are computed by every wave: no branch in the hot loop)
+        if (!MASK || t < wave_tiles) {
+            // Operands from LDS, issued ahead of their MFMAs: the 16-byte K rows of
+            // every k-step first, then the V^T transpose reads interleaved with the QK
+            // MFMAs, so their latency hides behind the QK product and the softmax.
+            u32x4 kop[NJB][NKK];
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
-            const uint16_t* kr0 = &k_lds[buf][(jb * 32 + n) * KLD + hg * (D / 2)];
+            for (int jb = 0; jb < NJB; ++jb) {
+                const uint16_t* kr0 = &k_lds[buf][(jb * 32 + n) * KLD + hg * (D / 2)];
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) kop[jb][kk] = load16(kr0 + kk * 8);
-        }
-        f32x16 s[NJB];
+                for (int kk = 0; kk < NKK; ++kk) kop[jb][kk] = load16(kr0 + kk * 8);
+            }
+            f32x16 s[NJB];
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) s[jb] = f32x16{};
+            for (int jb = 0; jb < NJB; ++jb) s[jb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+                    s[jb] = E::mfma32(as_vec8<T>(kop[jb][kk]), qf[kk], s[jb]);
+            // V^T operands: k-step st of block jb covers keys 16st + 8h + 4(lane/32) + e
+            // for operand slots 4h + e (the order the C layout of S^T leaves P in).
+            u32x4 vop[NDB][NJB][2];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+                        const int key0 = jb * 32 + 16 * st + 4 * (g16 >> 1) + e4;
+                        const int col = db * 32 + (g16 & 1) * 16 + 4 * q4;
+                        const u32x2 lo = lds_read_tr16(&v_lds[buf][key0 * VLD + col]);
+                        const u32x2 hi = lds_read_tr16(&v_lds[buf][(key0 + 8) * VLD + col]);
+                        vop[db][jb][st] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                    }
+            __builtin_amdgcn_sched_group_barrier(0x100, NJB * NKK, 0);  // K reads
+#pragma unroll
+            for (int i = 0; i < NJB * NKK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one QK MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDB * NJB * 2 / (NJB * NKK), 0);
+            }
+            if constexpr (MASK) {
+                // lane holds keys 8(i/4) + 4hg + i%4 of each 32-key block
+                const int kbase = t * BN;
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kbase + jb * 32 + 8 * (i >> 2) + hg * 4 + (i & 3);
+                        bool ok = key < Lk;
+                        if (CAUSAL) ok = ok && key <= row + diag;
+                        s[jb][i] = ok ? s[jb][i] : -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb)
-                s[jb] = E::mfma32(as_vec8<T>(kop[jb][kk]), qf[kk], s[jb]);
-        // V^T operands: k-step st of block jb covers keys 16st + 8h + 4(lane/32) + e
-        // for operand slots 4h + e (the order the C layout of S^T leaves P in).
-        u32x4 vop[NDB][NJB][2];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[jb][i]);
+            mx = fmaxf(mx, xor_shfl(mx, 32));
+            const float m_tile = mx == -INFINITY ? -INFINITY : mx * c - bias;
+            if (__any(m_tile > m_ref + kTau)) {
+                const float m_new = m_tile > m_ref + kTau ? m_tile : m_ref;
+                const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
+                m_ref = m_new;
+                l_run *= alpha;
 #pragma unroll
-            for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const int key0 = jb * 32 + 16 * st + 4 * (g16 >> 1) + e4;
-                    const int col = db * 32 + (g16 & 1) * 16 + 4 * q4;
-                    const u32x2 lo = lds_read_tr16(&v_lds[buf][key0 * VLD + col]);
-                    const u32x2 hi = lds_read_tr16(&v_lds[buf][(key0 + 8) * VLD + col]);
-                    vop[db][jb][st] = u32x4{lo.x, lo.y, hi.x, hi.y};
-                }
-        __builtin_amdgcn_sched_group_barrier(0x100, NJB * NKK, 0);  // K reads
-#pragma unroll
-        for (int i = 0; i < NJB * NKK; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one QK MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDB * NJB * 2 / (NJB * NKK), 0);
-        }
-        if constexpr (MASK) {
-            // lane holds keys 8(i/4) + 4hg + i%4 of each 32-key block
-            const int kbase = t * BN;
-#pragma unroll
-            for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kbase + jb * 32 + 8 * (i >> 2) + hg * 4 + (i & 3);
-                    bool ok = key < Lk;
-                    if (CAUSAL) ok = ok && key <= row + diag;
-                    s[jb][i] = ok ? s[jb][i] : -INFINITY;
-                }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[jb][i]);
-        mx = fmaxf(mx, xor_shfl(mx, 32));
-        const float m_tile = mx == -INFINITY ? -INFINITY : mx * c - bias;
-        if (__any(m_tile > m_ref + kTau)) {
-            const float m_new = m_tile > m_ref + kTau ? m_tile : m_ref;
-            const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
-            m_ref = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-        }
-        const float nb = -(bias + (m_ref == -INFINITY ? 0.f : m_ref));
+                for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+            }
+            const float nb = -(bias + (m_ref == -INFINITY ? 0.f : m_ref));
 
-        // p = 2^(s*c - bias - m_ref), packed to 16-bit as the B operand of PV
-        uint32_t pk[NJB][2][4];
-        float psum = 0.f;
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float p0 = fast_exp2(fmaf(s[jb][8 * st + 2 * j], c, nb));
-                    const float p1 = fast_exp2(fmaf(s[jb][8 * st + 2 * j + 1], c, nb));
-                    psum += p0 + p1;
-                    pk[jb][st][j] = E::pack2(p0, p1);
-                }
-        l_run += psum;
-
-        // O^T[d, row] += V^T[d, keys] P^T[keys, row]
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            // p = 2^(s*c - bias - m_ref), packed to 16-bit as the B operand of PV
+            uint32_t pk[NJB][2][4];
+            float psum = 0.f;
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const u32x4 bv = {pk[jb][st][0], pk[jb][st][1], pk[jb][st][2],
-                                      pk[jb][st][3]};
-                    o[db] = E::mfma32(as_vec8<T>(vop[db][jb][st]), as_vec8<T>(bv), o[db]);
-                }
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float p0 = fast_exp2(fmaf(s[jb][8 * st + 2 * j], c, nb));
+                        const float p1 = fast_exp2(fmaf(s[jb][8 * st + 2 * j + 1], c, nb));
+                        psum += p0 + p1;
+                        pk[jb][st][j] = E::pack2(p0, p1);
+                    }
+            l_run += psum;
 
+            // O^T[d, row] += V^T[d, keys] P^T[keys, row]
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+                        const u32x4 bv = {pk[jb][st][0], pk[jb][st][1], pk[jb][st][2],
+                                          pk[jb][st][3]};
+                        o[db] = E::mfma32(as_vec8<T>(vop[db][jb][st]), as_vec8<T>(bv), o[db]);
+                    }
+        }
         if (t + 1 < ntiles) {
             store_tile(buf ^ 1);
             if (t + 2 < ntiles) load_tile(t + 2, t + 2 >= full_tiles);
