@@ -91,13 +91,16 @@ size_t skv_workspace_bytes(int B_or_nseq, int Hkv, int D, int smooth_k) {
 int skv_pick_num_splits(int B, int Hkv, int rows_per_kv_head, int Lkv, int D) {
     (void)rows_per_kv_head;
     if (B <= 0 || Hkv <= 0 || Lkv <= 0) return 1;
-    // One or two work groups per compute unit (256 CUs) stream best: each then
-    // keeps several blocks in flight per wave, and a launch needs a single round of
-    // work groups.  Wide heads (D = 256) carry twice the bytes per key and do best
-    // with one.  Every chunk keeps at least 256 keys (two 32-key blocks per wave).
+    // One work group per compute unit (256 CUs) streams best: a launch then needs a
+    // single round of work groups (every round pays the latency chain of loading
+    // Q, the first blocks, the combine and the partial-state publish), and each wave
+    // keeps several blocks in flight.  Chunks longer than 4096 keys (D <= 128) are
+    // split once more, up to two work groups per CU.  Every chunk keeps at least 256
+    // keys (two 32-key blocks per wave).
     const int64_t units = (int64_t)B * Hkv;
-    const int64_t target = D >= 256 ? 256 : 512;
-    int64_t s = (target + units - 1) / units;
+    int64_t s = (256 + units - 1) / units;
+    if (D <= 128)
+        while (2 * s * units <= 512 && (Lkv + s - 1) / s > 4096) s *= 2;
     int64_t smax = Lkv / 256;
     if (smax < 1) smax = 1;
     if (s > smax) s = smax;

@@ -50,17 +50,21 @@ __device__ __forceinline__ void store_agent(float* p, float v) {
 // Single-launch decode: once a work group has written its chunk's partial state
 // (with store_agent) it waits for those stores to complete and takes a ticket for
 // its (batch, kv head); the last of the num_splits work groups to arrive merges
-// all partial states of those rows the stable way -- global max M of the chunk
-// LSEs, weights 2^(lse_s - M) -- after a device-scope acquire, writes the output
-// and its LSE, and returns the ticket counter to zero for the next call.
-// The merge keeps its memory latency off serial chains: all R x S partial LSEs
-// are fetched at once into LDS, and the output sum issues 8 part loads per wait.
-static_assert(16 * kMaxDecodeSplits + 32 <= SplitLds<64>::BYTES / 4, "merge weights fit in LDS");
-
+// all partial states of those rows, writes the output and its LSE, and returns the
+// ticket counter to zero for the next call.
+//
+// The merge keeps memory latency off serial chains: each thread owns Q adjacent
+// 4-column groups of one row and reads the partial LSEs and outputs of eight
+// chunks per round trip, all issued together.  Across groups of eight it keeps a
+// running max M of the chunk LSEs and rescales its sums by 2^(M_old - M_new) when M
+// grows; the result is the stable merge -- out = sum_s 2^(lse_s - M) o_s / sum_s
+// 2^(lse_s - M), lse = M + log2 of that sum -- with no exponent above 0.  Chunks
+// with lse = -inf get weight 0; if every chunk is -inf the row gets (0, -inf).
 template <typename T, int D>
-__device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, int R, int G,
-                                           float* scratch) {
+__device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, int R, int G) {
     using E = Elem<T>;
+    constexpr int Q = D / 64;          // 4-column groups per thread: 16 rows x D/4 / 256
+    constexpr int GS = 8;              // chunks per round trip
     __shared__ int is_last;
     const int tid = threadIdx.x, S = a.num_splits;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores are done
@@ -71,6 +75,10 @@ __device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, in
                   S - 1;
     __syncthreads();
     if (!is_last) return;
+    if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int r = tid * Q / (D / 4);   // the row this thread merges
+    if (r >= R) return;
+    const int d0 = (tid * Q % (D / 4)) * 4;
     // The partials are read with device-coherent (sc1) buffer loads, which miss any
     // stale line this XCD's L2 may hold, so no cache-wide invalidate is needed.
     // Byte offsets stay below 2^31 (checked on the host).
@@ -78,61 +86,59 @@ __device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, in
         __builtin_amdgcn_make_buffer_rsrc(a.out_part, (short)0, 0x7fffffff, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t pl_rsrc =
         __builtin_amdgcn_make_buffer_rsrc(a.lse_part, (short)0, 0x7fffffff, kBufferRsrcWord3);
-
+    const int h = hk * G + r / a.Lq, i = r % a.Lq;
+    const int64_t row_off = (int64_t)b * a.q_batch + (int64_t)h * a.q_head + (int64_t)i * a.q_row;
+    const int64_t lse_row = ((int64_t)b * a.Hq + h) * a.Lq + i;
     const int64_t lse_split = (int64_t)a.B * a.Hq * a.Lq;
-    float* wts = scratch;              // [R][S]: partial LSEs, then normalised weights
-    float* row_m = scratch + 16 * S;   // [R]: max
-    float* row_w = row_m + 16;         // [R]: sum of 2^(lse - max)
-    for (int idx = tid; idx < R * S; idx += 256) {
-        const int r = idx / S, sp = idx % S;
-        const int h = hk * G + r / a.Lq, i = r % a.Lq;
-        const int64_t e = sp * lse_split + ((int64_t)b * a.Hq + h) * a.Lq + i;
-        wts[idx] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(pl_rsrc, (int)(e * 4), 0, kCoherentLoad));
-    }
-    __syncthreads();
-    if (tid < R) {
-        float M = -INFINITY;
-        for (int sp = 0; sp < S; ++sp) M = fmaxf(M, wts[tid * S + sp]);
-        const float Mu = M == -INFINITY ? 0.f : M;
-        float W = 0.f;
-        for (int sp = 0; sp < S; ++sp) W += fast_exp2(wts[tid * S + sp] - Mu);
-        const float inv = W > 0.f ? 1.f / W : 0.f;
-        for (int sp = 0; sp < S; ++sp) wts[tid * S + sp] = fast_exp2(wts[tid * S + sp] - Mu) * inv;
-        row_m[tid] = M;
-        row_w[tid] = W;
-    }
-    __syncthreads();
 
-    for (int it = tid; it < 16 * (D / 4); it += 256) {
-        const int r = it / (D / 4), d = (it % (D / 4)) * 4;
-        if (r >= R) break;
-        const int h = hk * G + r / a.Lq, i = r % a.Lq;
-        const int64_t row_off = (int64_t)b * a.q_batch + (int64_t)h * a.q_head + (int64_t)i * a.q_row;
-        const int64_t op = row_off + d;  // element offset of split 0
-        const float* w = wts + r * S;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int sp0 = 0; sp0 < S; sp0 += 8) {
-            f32x4 x[8];
+    float M = -INFINITY, W = 0.f;
+    f32x4 acc[Q];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int64_t e = op + min(sp0 + u, S - 1) * a.part_stride;
-                x[u] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(po_rsrc, (int)(e * 4), 0, kCoherentLoad));
-            }
+    for (int q = 0; q < Q; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += GS) {
+        float l[GS];
+        f32x4 x[GS][Q];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc += x[u] * (sp0 + u < S ? w[sp0 + u] : 0.f);
+        for (int u = 0; u < GS; ++u) {
+            const int sp = min(s0 + u, S - 1);   // past S: a real chunk, weighted 0 below
+            l[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                pl_rsrc, (int)((sp * lse_split + lse_row) * 4), 0, kCoherentLoad));
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+                x[u][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    po_rsrc, (int)((row_off + d0 + 4 * q + sp * a.part_stride) * 4), 0,
+                    kCoherentLoad));
         }
-        u32x2 packed;
-        packed.x = E::pack2(acc[0], acc[1]);
-        packed.y = E::pack2(acc[2], acc[3]);
-        *reinterpret_cast<u32x2*>((uint16_t*)a.out + row_off + d) = packed;
-        if (d == 0 && a.lse) {
-            const float W = row_w[r];
-            a.lse[((int64_t)b * a.Hq + h) * a.Lq + i] = W > 0.f ? row_m[r] + fast_log2(W) : -INFINITY;
+        float mg = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < GS; ++u) {
+            if (s0 + u >= S) l[u] = -INFINITY;
+            mg = fmaxf(mg, l[u]);
         }
+        const float Mn = fmaxf(M, mg);
+        if (Mn == -INFINITY) continue;              // no chunk with a key so far
+        const float sc = fast_exp2(M - Mn);         // 0 while M is still -inf
+        W *= sc;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) acc[q] *= sc;
+#pragma unroll
+        for (int u = 0; u < GS; ++u) {
+            const float w = fast_exp2(l[u] - Mn);   // -inf chunks: 0
+            W += w;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) acc[q] += x[u][q] * w;
+        }
+        M = Mn;
     }
-    if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        u32x2 packed;
+        packed.x = E::pack2(acc[q][0] * inv, acc[q][1] * inv);
+        packed.y = E::pack2(acc[q][2] * inv, acc[q][3] * inv);
+        *reinterpret_cast<u32x2*>((uint16_t*)a.out + row_off + d0 + 4 * q) = packed;
+    }
+    if (d0 == 0 && a.lse) a.lse[lse_row] = W > 0.f ? M + fast_log2(W) : -INFINITY;
 }
 
 template <typename T, int D, bool FUSED>
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
             if (d == 0) *lp = lse_s;
         }
     }
-    if constexpr (FUSED) merge_tail<T, D>(a, b, hk, R, G, (float*)smem);
+    if constexpr (FUSED) merge_tail<T, D>(a, b, hk, R, G);
 }
 
 template <typename T, int D>
