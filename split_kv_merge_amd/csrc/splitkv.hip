@@ -25,12 +25,14 @@ namespace skv {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kKeysPerBlock = 32;
+// Keys per block: 32, or 16 at D = 256, where two 32-key blocks in flight per wave
+// (K and V, 128 registers each) would not leave room for a second wave per SIMD.
+template <int D> constexpr int keys_per_block() { return D == 256 ? 16 : 32; }
 
 template <int D> struct SplitLds {
     static constexpr int VLD = D + 16;  // V pitch (elements) in the staging slice
     static constexpr int OLD = D + 4;   // pitch (floats) of the combine buffer
-    static constexpr int STAGE = kWaves * kKeysPerBlock * VLD * 2;
+    static constexpr int STAGE = kWaves * keys_per_block<D>() * VLD * 2;
     static constexpr int COMB = kWaves * (16 * OLD + 32) * 4;
     static constexpr int BYTES = STAGE > COMB ? STAGE : COMB;
 };
@@ -142,13 +144,19 @@ __device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, in
 }
 
 template <typename T, int D, bool FUSED>
-__global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
+// Two waves per SIMD (two work groups per compute unit) at D <= 128: the second wave
+// hides the first one's load and LDS latencies; without the hint the compiler spends
+// registers down to one wave per SIMD.  D = 256 needs the whole register file.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+void splitkv_kernel(SplitArgs a) {
     using E = Elem<T>;
     typedef SplitLds<D> L;
     constexpr int NKK = D / 32;          // 16x16x32 k-steps over D
     constexpr int NDB = D / 16;          // 16-wide blocks of O^T
     constexpr int CPR = D / 8;           // 16-byte chunks per V row
-    constexpr int VCH = kKeysPerBlock * CPR / 64;  // V chunks per lane per block
+    constexpr int KPB = keys_per_block<D>();      // keys per block
+    constexpr int NHF = KPB / 16;                 // 16-key halves per block
+    constexpr int VCH = KPB * CPR / 64;           // V chunks per lane per block
     constexpr int VLD = L::VLD, OLD = L::OLD;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
     const int64_t j0l = min((int64_t)s * C, (int64_t)a.Lkv);
     const int j0 = (int)j0l;
     const int j1 = (int)min(j0l + C, (int64_t)a.Lkv);
-    const int nblk = (j1 - j0 + kKeysPerBlock - 1) / kKeysPerBlock;
+    const int nblk = (j1 - j0 + KPB - 1) / KPB;
 
     // Query row n of this kv head: head hk*G + n / Lq, position n % Lq.
     const bool r_ok = n < R;
@@ -186,12 +194,12 @@ __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
     // Loads of one block into a register buffer.  Rows past the chunk end are
     // clamped to its last key (real, finite data; the chunk is non-empty whenever a
     // block exists) and masked out of the softmax, so no load needs a branch.
-    typedef u32x4 KBuf[2][NKK];
+    typedef u32x4 KBuf[NHF][NKK];
     typedef u32x4 VBuf[VCH];
     auto load_block = [&](KBuf& kb_, VBuf& vb_, int blk) {
-        const int kb = j0 + blk * kKeysPerBlock;
+        const int kb = j0 + blk * KPB;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        for (int hf = 0; hf < NHF; ++hf) {
             const int j = min(kb + hf * 16 + n, j1 - 1);
             const uint16_t* kr = kp + (int64_t)j * a.kv_row + g4 * 8;
 #pragma unroll
@@ -210,23 +218,23 @@ __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
     for (int db = 0; db < NDB; ++db) o[db] = f32x4{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    uint16_t* vl = (uint16_t*)smem + wave * kKeysPerBlock * VLD;
+    uint16_t* vl = (uint16_t*)smem + wave * KPB * VLD;
     const int e4 = (lane & 15) >> 2, q4 = lane & 3;
 
     auto compute_block = [&](const KBuf& kc, const VBuf& vc, int blk) {
         // S^T for keys [16hf, 16hf + 16) of the block: lane holds keys 16hf + 4g4 + i.
-        f32x4 sv[2];
+        f32x4 sv[NHF];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        for (int hf = 0; hf < NHF; ++hf) {
             sv[hf] = f32x4{};
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk)
                 sv[hf] = E::mfma16(as_vec8<T>(kc[hf][kk]), qf[kk], sv[hf]);
         }
-        const int kb = j0 + blk * kKeysPerBlock;
+        const int kb = j0 + blk * KPB;
         float mx = -INFINITY;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
+        for (int hf = 0; hf < NHF; ++hf)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = kb + hf * 16 + 4 * g4 + i;
@@ -240,20 +248,22 @@ __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = fast_exp2(m_run - m_use);
         m_run = m_new;
+        // B operand: slot j <-> key 16(j/4) + 4g4 + j%4; with 16-key blocks the
+        // upper four slots hold 0, so the 32-key MFMA step adds nothing for them.
         float p[8];
         float psum = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(sv[j >> 2][j & 3] - m_use);
+            p[j] = (j >> 2) < NHF ? fast_exp2(sv[(j >> 2) % NHF][j & 3] - m_use) : 0.f;
             psum += p[j];
         }
         l_run = l_run * alpha + psum;
-        // B operand: slot j <-> key 16(j/4) + 4g4 + j%4
         const u32x4 pb = {E::pack2(p[0], p[1]), E::pack2(p[2], p[3]), E::pack2(p[4], p[5]),
                           E::pack2(p[6], p[7])};
 
-        // stage V (32 keys x D) in this wave's LDS slice, then V^T operands by
-        // transpose reads: slot 4h + e of lane (d, g4) is V[16h + 4g4 + e][d].
+        // stage V (KPB keys x D) in this wave's LDS slice, then V^T operands by
+        // transpose reads: slot 4h + e of lane (d, g4) is V[16h + 4g4 + e][d] (with
+        // 16-key blocks the upper slots repeat the lower keys, finite and weighted 0).
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
@@ -266,8 +276,11 @@ __global__ __launch_bounds__(256) void splitkv_kernel(SplitArgs a) {
             o[db] *= alpha;
             const int key0 = 4 * g4 + e4, col = db * 16 + 4 * q4;
             const u32x2 lo = lds_read_tr16(vl + key0 * VLD + col);
-            const u32x2 hi = lds_read_tr16(vl + (key0 + 16) * VLD + col);
-            const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
+            u32x4 av = {lo.x, lo.y, lo.x, lo.y};
+            if constexpr (NHF == 2) {
+                const u32x2 hi = lds_read_tr16(vl + (key0 + 16) * VLD + col);
+                av = u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
             o[db] = E::mfma16(as_vec8<T>(av), as_vec8<T>(pb), o[db]);
         }
         lds_wave_sync();
