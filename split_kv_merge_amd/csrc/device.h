@@ -38,6 +38,11 @@ template <> struct Elem<__bf16> {
     static __device__ __forceinline__ uint32_t pack2(float a, float b) {
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
     }
+    // acc + the two bf16 values of a packed pair (one v_dot2_f32_bf16 against 1, 1)
+    static __device__ __forceinline__ float sum2(uint32_t packed, float acc) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed),
+                                               bf16x2{(__bf16)1.f, (__bf16)1.f}, acc, false);
+    }
     // 32x32x16: A [32 x 16], B [16 x 32], 8 elements per lane each
     static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -58,6 +63,11 @@ template <> struct Elem<_Float16> {
     }
     static __device__ __forceinline__ uint32_t pack2(float a, float b) {
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+    }
+    // acc + the two fp16 values of a packed pair (one v_dot2_f32_f16 against 1, 1)
+    static __device__ __forceinline__ float sum2(uint32_t packed, float acc) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed),
+                                      f16x2{(_Float16)1.f, (_Float16)1.f}, acc, false);
     }
     static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);

@@ -292,9 +292,12 @@ void fmha_fwd_kernel(FmhaArgs a) {
             }
             const float nb = -(bias + (m_ref == -INFINITY ? 0.f : m_ref));
 
-            // p = 2^(s*c - bias - m_ref), packed to 16-bit as the B operand of PV
+            // p = 2^(s*c - bias - m_ref), packed to 16-bit as the B operand of PV.  The
+            // row sum adds the packed (rounded) pairs with one dot2 against (1, 1): the
+            // normaliser then sums exactly the P values the PV product uses.  Four
+            // partial sums keep the dependent chains short.
             uint32_t pk[NJB][2][4];
-            float psum = 0.f;
+            float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
@@ -303,10 +306,10 @@ void fmha_fwd_kernel(FmhaArgs a) {
                     for (int j = 0; j < 4; ++j) {
                         const float p0 = fast_exp2(fmaf(s[jb][8 * st + 2 * j], c, nb));
                         const float p1 = fast_exp2(fmaf(s[jb][8 * st + 2 * j + 1], c, nb));
-                        psum += p0 + p1;
                         pk[jb][st][j] = E::pack2(p0, p1);
+                        psum[j] = E::sum2(pk[jb][st][j], psum[j]);
                     }
-            l_run += psum;
+            l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
 
             // O^T[d, row] += V^T[d, keys] P^T[keys, row]
 #pragma unroll
