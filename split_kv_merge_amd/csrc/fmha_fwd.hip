@@ -43,7 +43,9 @@ template <int D> struct FmhaTile {
     static constexpr int NW = D == 256 ? 4 : 8;
     static constexpr int NT = 64 * NW;             // threads per work group
     static constexpr int BM = 32 * NW;             // query rows per work group
-    static constexpr int BN = D == 256 ? 32 : 64;  // keys per tile
+    // keys per tile: 128 at D = 64, where the softmax work per key is largest
+    // relative to the MFMA work and fewer, longer tiles give it more independence
+    static constexpr int BN = D == 256 ? 32 : (D == 64 ? 128 : 64);
     static constexpr int KLD = D + 8;              // K row pitch in LDS (elements)
     // V row pitch in LDS (elements): 16 dwords past a multiple of 64 banks, so each
     // 32-lane pass of the transpose read (4 rows x 2 column groups x 4 lanes x 2
