@@ -143,6 +143,26 @@ def test_varlen_parity(skv, causal, smooth_k):
     assert_out_close(out.cpu(), ro)
 
 
+@pytest.mark.parametrize("D,dtype,Hq,Hkv", [(64, "fp16", 8, 2), (256, "bf16", 4, 1)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_parity_other_heads(skv, D, dtype, Hq, Hkv, causal):
+    """Varlen at D = 64 (128-key tiles) and D = 256 (the 4-wave kernel), with smoothing
+    and GQA; lengths straddle the 128/256-row and 32/128-key tile edges."""
+    vl = wl.varlen_prefill(seed=43 + D, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, causal=causal,
+                           lengths=[3, 129, 255, 256, 257, 130, 1, 400])
+    ro, rl = oracle.attn_varlen(wl.bits(vl.q), wl.bits(vl.k), wl.bits(vl.v), dtype,
+                                vl.cu_seqlens_q, vl.cu_seqlens_k, vl.scale, causal)
+    q, k, v = _gpu(vl.q), _gpu(vl.k), _gpu(vl.v)
+    out = _poison(q.shape, q.dtype)
+    lse = _poison((q.shape[1], q.shape[0]), torch.float32)
+    skv.attn_fwd_varlen(q, k, v, _gpu(vl.cu_seqlens_q), _gpu(vl.cu_seqlens_k),
+                        max(vl.lengths), scale=vl.scale, causal=causal, smooth_k=True,
+                        out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert_lse_close(lse.cpu(), rl)
+    assert_out_close(out.cpu(), ro)
+
+
 # ------------------------------------------------------ split-KV + merge
 
 SPLIT_CASES = [
