@@ -167,6 +167,8 @@ def attn_fwd(q, k, v, scale=None, layout="HND", causal=False, smooth_k=False, re
     if out is None:
         out = torch.empty_like(q)
     _need_cuda_contig("out", out)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     if lse is not None:
@@ -207,6 +209,8 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=Non
     if out is None:
         out = torch.empty_like(q)
     _need_cuda_contig("out", out)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
     if return_lse and lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
     if lse is not None:
