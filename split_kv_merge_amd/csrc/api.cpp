@@ -135,6 +135,12 @@ skv_status_t skv_attn_fwd(const void* q, const void* k, const void* v, void* out
         if (workspace_bytes < need)
             return fail(SKV_EINVAL, "workspace has %zu bytes, smooth_k needs %zu", workspace_bytes, need);
     }
+    const int bm = skv::fmha_rows_per_block(D);
+    const int grid_m = (int)(((int64_t)Sq + bm - 1) / bm);
+    if (grid_m > 65535)
+        return fail(SKV_EUNSUPPORTED, "Sq=%d needs %d row tiles, over the 65535 grid limit", Sq, grid_m);
+    // (The kernels form K/V offsets inside a tile of at most 128 rows in 32 bits:
+    // 127 * Hkv * D + D < 2^31 for every Hkv <= Hq <= 65535 and D <= 256.)
     if (B == 0 || Sq == 0) return SKV_OK;
 
     hipStream_t s = (hipStream_t)stream;
@@ -159,10 +165,6 @@ skv_status_t skv_attn_fwd(const void* q, const void* k, const void* v, void* out
         if (st != SKV_OK) return st;
         a.kbar = (const float*)workspace;
     }
-    const int bm = skv::fmha_rows_per_block(D);
-    const int grid_m = (int)(((int64_t)Sq + bm - 1) / bm);
-    if (grid_m > 65535)
-        return fail(SKV_EUNSUPPORTED, "Sq=%d needs %d row tiles, over the 65535 grid limit", Sq, grid_m);
     return launched(skv::launch_fmha(a, dtype, D, causal != 0, false, grid_m, B, s), "fmha_fwd");
 }
 
@@ -200,6 +202,11 @@ skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
         if (workspace_bytes < need)
             return fail(SKV_EINVAL, "workspace has %zu bytes, smooth_k needs %zu", workspace_bytes, need);
     }
+    const int bm = skv::fmha_rows_per_block(D);
+    const int grid_m = (max_seqlen_q + bm - 1) / bm;
+    if (grid_m > 65535)
+        return fail(SKV_EUNSUPPORTED, "max_seqlen_q=%d needs %d row tiles, over the 65535 grid limit",
+                    max_seqlen_q, grid_m);
     if (nseq == 0 || total_q == 0 || max_seqlen_q == 0) return SKV_OK;
 
     hipStream_t s = (hipStream_t)stream;
@@ -219,11 +226,6 @@ skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
         if (st != SKV_OK) return st;
         a.kbar = (const float*)workspace;
     }
-    const int bm = skv::fmha_rows_per_block(D);
-    const int grid_m = (max_seqlen_q + bm - 1) / bm;
-    if (grid_m > 65535)
-        return fail(SKV_EUNSUPPORTED, "max_seqlen_q=%d needs %d row tiles, over the 65535 grid limit",
-                    max_seqlen_q, grid_m);
     return launched(skv::launch_fmha(a, dtype, D, causal != 0, true, grid_m, nseq, s), "fmha_fwd_varlen");
 }
 

@@ -95,6 +95,14 @@ def test_attn_fwd_rejects(lib, kw, status):
     assert lib.skv_last_error() != b""
 
 
+def test_grid_limit_rejected_before_any_launch(lib):
+    """Too many row tiles is refused before anything is launched, also with smoothing,
+    whose mean-k kernel would otherwise run first and write the workspace."""
+    ws = dict(smooth_k=1, ws=FAKE, ws_bytes=1 << 20)
+    assert _fwd(lib, Sq=65536 * 256, **ws) == 2
+    assert b"row tiles" in lib.skv_last_error()
+
+
 def test_zero_sized_calls_succeed_without_launching(lib):
     assert _fwd(lib, B=0) == 0
     assert _fwd(lib, Sq=0) == 0
