@@ -20,8 +20,9 @@ overhead does not open gaps).  The two-kernel form (partials, then merge_state)
 is timed as well and reported per problem.
 `cpu_baseline` times the fp64 oracle (oracle/, C + OpenMP) on a bounded sample of
 the same workload.  `secondary` reports the other shapes of the same path
-(wide-head decode, varlen causal prefill, ring-style chunked prefill, the tiny
-LSE case) in us, GB/s or TFLOP/s and as a fraction of the roofline.
+(the decode on a partly filled KV cache bounded by a device kv_len, wide-head
+decode, varlen causal prefill, ring-style chunked prefill, the tiny LSE case) in
+us, GB/s or TFLOP/s and as a fraction of the roofline.
 """
 from __future__ import annotations
 
@@ -276,10 +277,27 @@ def cpu_baseline(dec, args):
                 cpu=platform.processor() or platform.machine())
 
 
-def secondary(skv, args):
+def secondary(skv, args, dec):
     import workloads as wl
     res = {}
     reps = 20
+
+    # partly filled KV cache: the Lkv-32768 decode_gqa problem with every kv_len = 4096
+    # (lengths on the device, split count chosen for the capacity, as a captured
+    # serving loop would keep it); only the filled keys are read
+    d32 = dec[-1]
+    B, Hq, Hkv, Lq, Lkv, D = d32.dims
+    filled = 4096
+    kvl = torch.full((B,), filled, dtype=torch.int32, device="cuda")
+
+    def partly_filled():
+        skv.attn_splitkv_decode(d32.q, d32.k, d32.v, num_splits=d32.S, scale=d32.scale,
+                                out=d32.out, lse=d32.lse, workspace=d32.ws, kv_len=kvl)
+    us = kernel_durations([partly_filled], reps)[0]
+    fb = 2 * B * Hkv * filled * D * 2 + 2 * B * Hq * Lq * D * 2 + B * Hq * Lq * 4
+    res["decode_gqa_capacity32768_kvlen4096"] = dict(
+        us=round(us, 2), gbs=round(fb / (us * 1e-6) / 1e9, 1), num_splits=d32.S,
+        filled_bytes=fb)
 
     # wide-head decode: B4 Hq16 Hkv4 Lq4 D256, K offset +2; the two problems
     # alternate, so each reads what the other evicted
@@ -407,7 +425,7 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(dec, args)
-    sec = {} if args.no_secondary else secondary(skv, args)
+    sec = {} if args.no_secondary else secondary(skv, args, dec)
     copy_probe()
     line = {
         "metric": METRIC,

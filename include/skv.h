@@ -123,10 +123,19 @@ skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
  *       own softmax sum.
  *   lse_part float32 [num_splits, B, Hq, Lq]: chunk s's LSE (log2).
  *
- * Chunk s covers keys [s*C, min((s+1)*C, Lkv)) with C = ceil(Lkv / num_splits).
- * Every slot of both buffers is written, including chunks that hold no key, which
- * get (0, -inf) [ET reviewer item 3: no early exit for empty splits], so neither
- * buffer needs initialising.  Merge the states with skv_merge_state.
+ *   kv_len DEVICE int32 [B] or NULL: the filled length of each batch element's KV
+ *       cache [ET docstring diff: only the filled positions are swept, O(context)
+ *       instead of O(max_seq_len), read on the device and graph-safe; NULL sweeps
+ *       the full Lkv].  Keys at or past kv_len[b] are never read (they may hold
+ *       anything, NaN included).  Values are read in the kernel, not validated on
+ *       the host; each is clamped to [0, Lkv].
+ *
+ * With N_b = Lkv (or the clamped kv_len[b]), chunk s of batch element b covers keys
+ * [s*C_b, min((s+1)*C_b, N_b)) with C_b = ceil(N_b / num_splits): the chunks split
+ * the filled length evenly.  Every slot of both buffers is written, including
+ * chunks that hold no key, which get (0, -inf) [ET reviewer item 3: no early exit
+ * for empty splits], so neither buffer needs initialising.  Merge the states with
+ * skv_merge_state.
  * Limits: Lq >= 1, Lkv >= 0, num_splits >= 1, (Hq / Hkv) * Lq <= 16
  * (SKV_EUNSUPPORTED beyond).
  */
@@ -134,7 +143,7 @@ skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* 
                                       float* out_part, float* lse_part, int B, int Hq,
                                       int Hkv, int Lq, int Lkv, int D, skv_dtype_t dtype,
                                       skv_layout_t layout, float scale, int num_splits,
-                                      void* stream);
+                                      const int32_t* kv_len, void* stream);
 
 /*
  * Split-KV decode in one launch: the partial states of skv_attn_splitkv_partial
@@ -143,7 +152,7 @@ skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* 
  * per-split softmax and global-max rescale; reviewer item 2: keep the reduce off
  * a separate serial path].
  *
- *   q, k, v, layout, num_splits: as skv_attn_splitkv_partial; num_splits <= 256
+ *   q, k, v, layout, num_splits, kv_len: as skv_attn_splitkv_partial; num_splits <= 256
  *       and num_splits*B*Hq*Lq*D*4 < 2^31 bytes of partial states (SKV_EUNSUPPORTED
  *       beyond).
  *   out  q's shape, layout and dtype: the merged output.
@@ -158,8 +167,8 @@ skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* 
 skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v, void* out,
                                      float* lse, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
                                      skv_dtype_t dtype, skv_layout_t layout, float scale,
-                                     int num_splits, void* workspace, size_t workspace_bytes,
-                                     void* stream);
+                                     int num_splits, const int32_t* kv_len, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* Workspace bytes of skv_attn_splitkv_decode (0 for non-positive sizes). */
 size_t skv_splitkv_workspace_bytes(int B, int Hq, int Lq, int D, int num_splits, int Hkv);

@@ -59,9 +59,9 @@ def _load():
     lib.skv_attn_fwd.restype = I
     lib.skv_attn_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P, SZ, P]
     lib.skv_attn_fwd_varlen.restype = I
-    lib.skv_attn_splitkv_partial.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
+    lib.skv_attn_splitkv_partial.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P]
     lib.skv_attn_splitkv_partial.restype = I
-    lib.skv_attn_splitkv_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
+    lib.skv_attn_splitkv_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, SZ, P]
     lib.skv_attn_splitkv_decode.restype = I
     lib.skv_splitkv_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.skv_splitkv_workspace_bytes.restype = SZ
@@ -121,6 +121,15 @@ def _need_cuda_contig(name, t):
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _check_kv_len(kv_len, B):
+    """kv_len: None, or an int32 GPU tensor of B filled lengths (read on the device)."""
+    if kv_len is None:
+        return
+    _need_cuda_contig("kv_len", kv_len)
+    if kv_len.dtype != torch.int32 or tuple(kv_len.shape) != (B,):
+        raise ValueError(f"kv_len must be an int32 tensor of shape ({B},)")
 
 
 def workspace_bytes(b_or_nseq: int, hkv: int, d: int, smooth_k: bool) -> int:
@@ -228,10 +237,12 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=Non
 
 
 def attn_splitkv_partial(q, k, v, num_splits=None, scale=None, layout="HND", out_part=None,
-                         lse_part=None):
+                         lse_part=None, kv_len=None):
     """Split-KV decode partials: returns (out_part float32 [S, *q.shape],
     lse_part float32 [S, B, Hq, Lq]) for S = num_splits chunks of the keys
-    (default: pick_num_splits)."""
+    (default: pick_num_splits).  ``kv_len`` (int32 GPU tensor [B], optional): the
+    filled KV length per batch element; only those keys are read, split evenly
+    over the chunks."""
     lib = _load()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _need_cuda_contig(n, t)
@@ -240,6 +251,7 @@ def attn_splitkv_partial(q, k, v, num_splits=None, scale=None, layout="HND", out
     B, Hq, Hkv, Lq, Lkv, D = _dims(q, k, layout)
     if Hkv <= 0 or Hq % Hkv:
         raise ValueError(f"Hq ({Hq}) must be a multiple of Hkv ({Hkv})")
+    _check_kv_len(kv_len, B)
     if num_splits is None:
         num_splits = pick_num_splits(B, Hkv, (Hq // Hkv) * Lq, Lkv, D)
     if scale is None:
@@ -258,7 +270,7 @@ def attn_splitkv_partial(q, k, v, num_splits=None, scale=None, layout="HND", out
     _check(lib.skv_attn_splitkv_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(out_part), _ptr(lse_part),
                                         B, Hq, Hkv, Lq, Lkv, D, _dt(q),
                                         SKV_HND if layout == "HND" else SKV_NHD, float(scale), S,
-                                        _stream(q.device)))
+                                        _ptr(kv_len), _stream(q.device)))
     return out_part, lse_part
 
 
@@ -267,13 +279,14 @@ def splitkv_workspace_bytes(B: int, Hq: int, Lq: int, D: int, num_splits: int, H
 
 
 def attn_splitkv_decode(q, k, v, num_splits=None, scale=None, layout="HND", out=None, lse=None,
-                        workspace=None, return_lse=True):
+                        workspace=None, return_lse=True, kv_len=None):
     """Split-KV decode in one launch (partials + stable merge): returns (out, lse) with
     out in q's shape and dtype and lse float32 [B, Hq, Lq] (log2).
 
     ``workspace`` (uint8 GPU tensor of splitkv_workspace_bytes(...) bytes) must be
     zero-filled before its first use; the call leaves it zero-filled again, so it can
     be reused by later calls and graph replays.  A fresh zeroed one is made if None.
+    ``kv_len``: as in attn_splitkv_partial.
     """
     lib = _load()
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -283,6 +296,7 @@ def attn_splitkv_decode(q, k, v, num_splits=None, scale=None, layout="HND", out=
     B, Hq, Hkv, Lq, Lkv, D = _dims(q, k, layout)
     if Hkv <= 0 or Hq % Hkv:
         raise ValueError(f"Hq ({Hq}) must be a multiple of Hkv ({Hkv})")
+    _check_kv_len(kv_len, B)
     if num_splits is None:
         num_splits = pick_num_splits(B, Hkv, (Hq // Hkv) * Lq, Lkv, D)
     if scale is None:
@@ -306,7 +320,7 @@ def attn_splitkv_decode(q, k, v, num_splits=None, scale=None, layout="HND", out=
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.skv_attn_splitkv_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv,
                                        Lq, Lkv, D, _dt(q), SKV_HND if layout == "HND" else SKV_NHD,
-                                       float(scale), S, _ptr(workspace), ws_bytes,
+                                       float(scale), S, _ptr(kv_len), _ptr(workspace), ws_bytes,
                                        _stream(q.device)))
     return (out, lse) if lse is not None else out
 

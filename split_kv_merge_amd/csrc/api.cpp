@@ -236,7 +236,8 @@ namespace {
 // Validation and argument block shared by the two split-KV entry points.
 skv_status_t prepare_split(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
                            int Lq, int Lkv, int D, skv_dtype_t dtype, skv_layout_t layout,
-                           float scale, int num_splits, skv::SplitArgs& a) {
+                           float scale, int num_splits, const int32_t* kv_len,
+                           skv::SplitArgs& a) {
     if (!q) return fail(SKV_EINVAL, "q must be non-NULL");
     if ((!k || !v) && Lkv > 0) return fail(SKV_EINVAL, "k and v must be non-NULL when Lkv > 0");
     if (B < 0 || Lq < 1 || Lkv < 0)
@@ -251,6 +252,7 @@ skv_status_t prepare_split(const void* q, const void* k, const void* v, int B, i
                     (long long)(Hq / Hkv) * Lq);
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
         return fail(SKV_EINVAL, "q, k and v must be 16-byte aligned");
+    if (kv_len && !aligned(kv_len, 4)) return fail(SKV_EINVAL, "kv_len must be 4-byte aligned");
     if (B > 65535 || Hkv > 65535) return fail(SKV_EUNSUPPORTED, "B or Hkv exceeds the 65535 grid limit");
     if (!elems_ok({num_splits, B, Hq, Lq, D}) || !elems_ok({B, Hkv, Lkv, D}))
         return fail(SKV_EINVAL, "tensor sizes overflow 64-bit indexing");
@@ -258,6 +260,7 @@ skv_status_t prepare_split(const void* q, const void* k, const void* v, int B, i
     a = skv::SplitArgs{};
     a.q = q; a.k = k; a.v = v;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lkv = Lkv; a.num_splits = num_splits;
+    a.kv_len = kv_len;
     a.q_row = hnd ? D : (int64_t)Hq * D;
     a.q_head = hnd ? (int64_t)Lq * D : D;
     a.q_batch = (int64_t)Hq * Lq * D;
@@ -279,12 +282,12 @@ skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* 
                                       float* out_part, float* lse_part, int B, int Hq,
                                       int Hkv, int Lq, int Lkv, int D, skv_dtype_t dtype,
                                       skv_layout_t layout, float scale, int num_splits,
-                                      void* stream) {
+                                      const int32_t* kv_len, void* stream) {
     clear_err();
     if (!out_part || !lse_part) return fail(SKV_EINVAL, "out_part and lse_part must be non-NULL");
     skv::SplitArgs a;
     skv_status_t st = prepare_split(q, k, v, B, Hq, Hkv, Lq, Lkv, D, dtype, layout, scale,
-                                    num_splits, a);
+                                    num_splits, kv_len, a);
     if (st != SKV_OK) return st;
     if (!aligned(out_part, 16)) return fail(SKV_EINVAL, "out_part must be 16-byte aligned");
     if (!aligned(lse_part, 4)) return fail(SKV_EINVAL, "lse_part must be 4-byte aligned");
@@ -304,13 +307,13 @@ size_t skv_splitkv_workspace_bytes(int B, int Hq, int Lq, int D, int num_splits,
 skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v, void* out,
                                      float* lse, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
                                      skv_dtype_t dtype, skv_layout_t layout, float scale,
-                                     int num_splits, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+                                     int num_splits, const int32_t* kv_len, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
     clear_err();
     if (!out) return fail(SKV_EINVAL, "out must be non-NULL");
     skv::SplitArgs a;
     skv_status_t st = prepare_split(q, k, v, B, Hq, Hkv, Lq, Lkv, D, dtype, layout, scale,
-                                    num_splits, a);
+                                    num_splits, kv_len, a);
     if (st != SKV_OK) return st;
     if (!aligned(out, 16)) return fail(SKV_EINVAL, "out must be 16-byte aligned");
     if (lse && !aligned(lse, 4)) return fail(SKV_EINVAL, "lse must be 4-byte aligned");

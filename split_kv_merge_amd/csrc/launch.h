@@ -42,6 +42,9 @@ struct SplitArgs {
     float* out_part;
     float* lse_part;
     int B, Hq, Hkv, Lq, Lkv, num_splits;
+    // filled KV length per batch element (device, nullable: NULL = Lkv for all);
+    // read in the kernel and clamped to [0, Lkv]
+    const int32_t* kv_len;
     int64_t q_row, q_head, q_batch;
     int64_t kv_row, kv_head, kv_batch;
     int64_t part_stride;        // elements between consecutive splits of out_part

@@ -166,11 +166,16 @@ void splitkv_kernel(SplitArgs a) {
     const int s = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     const int G = a.Hq / a.Hkv, R = G * a.Lq;
 
-    // chunk [j0, j1) of this split
-    const int64_t C = ((int64_t)a.Lkv + a.num_splits - 1) / a.num_splits;
-    const int64_t j0l = min((int64_t)s * C, (int64_t)a.Lkv);
+    // Chunk [j0, j1) of this split.  The keys this batch element holds are Lkv, or its
+    // filled length kv_len[b] (read on the device, so a captured graph follows the
+    // length from replay to replay); the S chunks split that length evenly, so the
+    // work stays spread over all of them.
+    int nkeys = a.Lkv;
+    if (a.kv_len) nkeys = min(max(a.kv_len[b], 0), a.Lkv);
+    const int64_t C = ((int64_t)nkeys + a.num_splits - 1) / a.num_splits;
+    const int64_t j0l = min((int64_t)s * C, (int64_t)nkeys);
     const int j0 = (int)j0l;
-    const int j1 = (int)min(j0l + C, (int64_t)a.Lkv);
+    const int j1 = (int)min(j0l + C, (int64_t)nkeys);
     const int nblk = (j1 - j0 + KPB - 1) / KPB;
 
     // Query row n of this kv head: head hk*G + n / Lq, position n % Lq.

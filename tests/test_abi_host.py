@@ -129,16 +129,18 @@ def test_splitkv_rejects(lib):
     P = FAKE
 
     def call(**kw):
-        a = dict(B=1, Hq=32, Hkv=8, Lq=1, Lkv=64, D=128, S=4)
+        a = dict(B=1, Hq=32, Hkv=8, Lq=1, Lkv=64, D=128, S=4, kv_len=None)
         a.update(kw)
         return lib.skv_attn_splitkv_partial(P, P, P, P, P, a["B"], a["Hq"], a["Hkv"], a["Lq"],
-                                            a["Lkv"], a["D"], 0, 0, 0.1, a["S"], None)
+                                            a["Lkv"], a["D"], 0, 0, 0.1, a["S"], a["kv_len"],
+                                            None)
     assert call(S=0) == 1
     assert call(Lq=0) == 1
     assert call(Lkv=-1) == 1
     assert call(Hq=30) == 1
     assert call(Lq=5) == 2           # (32/8)*5 = 20 rows per kv head > 16
     assert call(D=80) == 2
+    assert call(kv_len=ctypes.c_void_p(0x10002)) == 1   # kv_len misaligned
     assert call(B=0) == 0
 
 
@@ -184,12 +186,14 @@ def test_splitkv_decode_rejects(lib):
     ws = ctypes.c_void_p(0x20000)   # 256-byte aligned
 
     def call(**kw):
-        a = dict(B=2, Hq=32, Hkv=8, Lq=1, Lkv=4096, D=128, S=8, ws=ws, wsb=1 << 30, out=P)
+        a = dict(B=2, Hq=32, Hkv=8, Lq=1, Lkv=4096, D=128, S=8, ws=ws, wsb=1 << 30, out=P,
+                 kv_len=None)
         a.update(kw)
         return lib.skv_attn_splitkv_decode(P, P, P, a["out"], None, a["B"], a["Hq"], a["Hkv"],
-                                           a["Lq"], a["Lkv"], a["D"], 0, 0, 0.1, a["S"], a["ws"],
-                                           a["wsb"], None)
-    assert call(S=257) == 2          # the merge keeps S weights per row in LDS
+                                           a["Lq"], a["Lkv"], a["D"], 0, 0, 0.1, a["S"],
+                                           a["kv_len"], a["ws"], a["wsb"], None)
+    assert call(S=257) == 2          # at most 256 splits in the single-launch form
+    assert call(kv_len=ctypes.c_void_p(0x10001)) == 1   # kv_len misaligned
     assert call(ws=None) == 1
     assert call(ws=ctypes.c_void_p(0x20010)) == 1     # not 256-byte aligned
     assert call(wsb=16) == 1
