@@ -63,6 +63,12 @@ def _load():
     lib.oracle_splitkv_partials.restype = I
     lib.oracle_merge.argtypes = [I, I64, I, P, P, P, P]
     lib.oracle_merge.restype = None
+    lib.oracle_sage_kbar.argtypes = [P, I, I, I, I, I, I, P]
+    lib.oracle_sage_kbar.restype = None
+    lib.oracle_sage_quant.argtypes = [P, I, I, I, I, I, I, P, P, P]
+    lib.oracle_sage_quant.restype = I
+    lib.oracle_sage_attn.argtypes = [P, P, P, I, I, I, I, I, I, I, I, D, I, I, P, I64, P, P]
+    lib.oracle_sage_attn.restype = I
     _lib = lib
     return lib
 
@@ -228,4 +234,93 @@ def merge(o_parts, lse_parts):
     out = np.empty(o.shape[1:], np.float64)
     lse = np.empty(l.shape[1:], np.float64)
     _load().oracle_merge(S, R, D, _ptr(o), _ptr(l), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+# ----------------------------------------------------- INT8 QK^T (Sage-v1 reading)
+
+SAGE_BLOCK = 32  # rows (query rows or keys) per quantisation block
+
+
+def sage_kbar(k, dtype, layout="HND") -> np.ndarray:
+    """mean(k) over keys per (batch, kv head), exact then rounded to float32 [B, Hkv, D]."""
+    k = _u16(k)
+    if _lay(layout) == HND:
+        B, Hkv, Sk, D = k.shape
+    else:
+        B, Sk, Hkv, D = k.shape
+    out = np.empty((B, Hkv, D), np.float32)
+    _load().oracle_sage_kbar(_ptr(k), _dt(dtype), _lay(layout), B, Hkv, Sk, D, _ptr(out))
+    return out
+
+
+def sage_quant_tensor(x, dtype, layout="HND", center=None):
+    """Per-block INT8 codes of x (minus center [B,H,D] float32 if given).
+
+    Returns (codes int8 [B,H,S,D] in HND order, scales float32 [B,H,ceil(S/32)]).
+    """
+    x = _u16(x)
+    if x.ndim != 4:
+        raise ValueError("x must be 4-D")
+    if _lay(layout) == HND:
+        B, H, S, D = x.shape
+    else:
+        B, S, H, D = x.shape
+    nb = (S + SAGE_BLOCK - 1) // SAGE_BLOCK
+    codes = np.empty((B, H, S, D), np.int8)
+    scales = np.empty((B, H, nb), np.float32)
+    c = None
+    if center is not None:
+        c = np.ascontiguousarray(np.asarray(center, np.float32))
+        if c.shape != (B, H, D):
+            raise ValueError("center must be [B, H, D]")
+    rc = _load().oracle_sage_quant(_ptr(x), _dt(dtype), _lay(layout), B, H, S, D,
+                                   _ptr(c) if c is not None else None, _ptr(codes),
+                                   _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle_sage_quant rejected its arguments")
+    return codes, scales
+
+
+def sage_quant(q, k, dtype, layout="HND", smooth_k=True):
+    """The quantisation step of the INT8 path.
+
+    Returns dict(q_codes, q_scale, k_codes, k_scale, kbar) with kbar float32
+    [B, Hkv, D] (zeros without smoothing); codes are HND-ordered int8.
+    """
+    q, k = _u16(q), _u16(k)
+    B, Hq, Hkv, Sq, Sk, D = _dims(q, k, layout)
+    kbar = sage_kbar(k, dtype, layout) if smooth_k else np.zeros((B, Hkv, D), np.float32)
+    qc, qs = sage_quant_tensor(q, dtype, layout)
+    kc, ks = sage_quant_tensor(k, dtype, layout, kbar if smooth_k else None)
+    return dict(q_codes=qc, q_scale=qs, k_codes=kc, k_scale=ks, kbar=kbar)
+
+
+def sage_attn(q, k, v, dtype, layout="HND", scale=None, causal=False, smooth_k=True, rows=None):
+    """INT8-QK^T attention: (out float64, lse float64 in log2 with the add-back).
+
+    rows=None: out in q's layout and lse [B, Hq, Sq]; else rows is an int array of
+    (b, h, i) triples and out is [n, D], lse [n].
+    """
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Hq, Hkv, Sq, Sk, D = _dims(q, k, layout)
+    if v.shape != k.shape:
+        raise ValueError("v must have k's shape")
+    if scale is None:
+        scale = float(np.float32(D ** -0.5))
+    if rows is None:
+        r, n = None, 0
+        out = np.empty(q.shape, np.float64)
+        lse = np.empty((B, Hq, Sq), np.float64)
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, np.int64).reshape(-1, 3))
+        n = r.shape[0]
+        out = np.empty((n, D), np.float64)
+        lse = np.empty((n,), np.float64)
+    rc = _load().oracle_sage_attn(_ptr(q), _ptr(k), _ptr(v), _dt(dtype), _lay(layout), B, Hq,
+                                  Hkv, Sq, Sk, D, float(scale), int(bool(causal)),
+                                  int(bool(smooth_k)), _ptr(r) if r is not None else None, n,
+                                  _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_sage_attn rejected its arguments")
     return out, lse

@@ -407,3 +407,197 @@ void oracle_merge(int S, int64_t R, int D, const double* o_parts, const double* 
         lse[r] = M + log2(wsum);
     }
 }
+
+/* ------------------------------------------- INT8 QK^T with smoothing (Sage-v1) */
+
+/*
+ * [P1] lists two INT8 attention variants beside the plain one, ark.sagev1 and
+ * ark.sageattn with kernel "v1_pvhalf" (task statement; Reproduction Steps,
+ * the apis table), says smooth_k is on by default for both (Problem
+ * Description, second issue), and fixes what their LSE must be: log2 of the
+ * sum of exp over the ORIGINAL unsmoothed scaled logits, i.e. the smoothed
+ * LSE plus scale * q . mean(k) / ln 2 (Reproduction Steps part 3).  It does not
+ * spell out the quantisation; this file takes the plainest reading of an INT8
+ * QK^T with smoothing, listed in the design notes:
+ *
+ *   1. kbar[b,g,:] = the mean of k over the call's keys, exact (fp64 sum of
+ *      the decoded values, divided by the key count) and rounded once to
+ *      float32; without smoothing kbar = 0.
+ *   2. K~ = fl32(k - kbar) elementwise in float32; Q is used as given.
+ *   3. Both are cut into blocks of SAGE_BLOCK consecutive rows (query rows or
+ *      keys) per (batch, head), all D columns; the last block may be short.
+ *      For a block X with a = max |x|:  delta = fl32(a / 127),
+ *      iota = a > 0 ? fl32(127 / a) : 0,  code(x) = rint(fl32(x * iota))
+ *      (round half to even), so codes lie in [-127, 127] and x ~ delta*code.
+ *   4. logits in log2 units: t_ij = scale * dQ(i) * dK(j) * (q^_i . k^_j) / ln 2,
+ *      the integer dot product taken exactly.
+ *   5. out_i = sum_j 2^t_ij v_j / sum_j 2^t_ij over the visible keys, and
+ *      lse_i = log2 sum_j 2^t_ij + scale * (q_i . kbar) / ln 2.
+ *
+ * Every float32 step (the subtraction, the two divisions, the product and the
+ * rounding) is written as a separate IEEE single-precision operation so the
+ * integer codes are fixed bit for bit; everything after the integer dot
+ * product is fp64.  The fp16 P.V of "v1_pvhalf" is the kernel's precision,
+ * not part of what is computed: out here uses v exactly.
+ */
+#define SAGE_BLOCK 32
+
+/* kbar of (b, g) as float32: fp64 sum over the Sk keys, one division, one rounding. */
+void oracle_sage_kbar(const uint16_t* k, int dtype, int layout, int B, int Hkv, int Sk, int D,
+                      float* kbar /* [B, Hkv, D] */) {
+    double* acc = (double*)malloc(sizeof(double) * (D > 0 ? D : 1));
+    if (!acc) return;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t g = 0; g < Hkv; ++g) {
+            kmean_range(k, dtype, layout, b, g, Hkv, Sk, D, 0, Sk, acc);
+            for (int d = 0; d < D; ++d) kbar[(b * Hkv + g) * D + d] = (float)acc[d];
+        }
+    free(acc);
+}
+
+/* One block quantiser on float32 values x[n] (step 3).  Writes codes and returns delta. */
+static float sage_quant_block(const float* x, int64_t n, int8_t* codes) {
+    float a = 0.f;
+    for (int64_t e = 0; e < n; ++e) {
+        float m = fabsf(x[e]);
+        if (m > a) a = m;
+    }
+    volatile float delta = a / 127.f;
+    volatile float iota = a > 0.f ? 127.f / a : 0.f;
+    for (int64_t e = 0; e < n; ++e) {
+        volatile float y = x[e] * iota;
+        float c = rintf(y);
+        if (c > 127.f) c = 127.f;
+        if (c < -127.f) c = -127.f;
+        codes[e] = (int8_t)c;
+    }
+    return delta;
+}
+
+/*
+ * Quantise a [B,H,S,D] (HND) or [B,S,H,D] (NHD) tensor of raw 16-bit patterns,
+ * minus center[b,h,:] (float32, nullable), per block of SAGE_BLOCK rows.
+ * codes is [B,H,S,D] int8 in HND order; scales is [B,H,ceil(S/SAGE_BLOCK)].
+ * Returns 0, or -1 on bad arguments / no memory.
+ */
+int oracle_sage_quant(const uint16_t* x, int dtype, int layout, int B, int H, int S, int D,
+                      const float* center, int8_t* codes, float* scales) {
+    if (B < 0 || H <= 0 || S < 0 || D <= 0) return -1;
+    const int64_t nblk = ((int64_t)S + SAGE_BLOCK - 1) / SAGE_BLOCK;
+    float* buf = (float*)malloc(sizeof(float) * SAGE_BLOCK * (size_t)D);
+    if (!buf) return -1;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t blk = 0; blk < nblk; ++blk) {
+                const int64_t i0 = blk * SAGE_BLOCK;
+                const int64_t i1 = i0 + SAGE_BLOCK < S ? i0 + SAGE_BLOCK : S;
+                for (int64_t i = i0; i < i1; ++i) {
+                    const uint16_t* xi = x + row_offset(layout, b, h, i, H, S, D);
+                    for (int d = 0; d < D; ++d) {
+                        volatile float v = (float)decode(xi[d], dtype);   /* exact */
+                        if (center) v = v - center[(b * H + h) * D + d];
+                        buf[(i - i0) * D + d] = v;
+                    }
+                }
+                scales[(b * H + h) * nblk + blk] =
+                    sage_quant_block(buf, (i1 - i0) * D, codes + ((b * H + h) * S + i0) * D);
+            }
+    free(buf);
+    return 0;
+}
+
+/*
+ * INT8 attention (steps 1-5) for every row (rows == NULL: out in q's layout, lse
+ * [B,Hq,Sq]) or for n chosen (b, h, i) triples (out [n, D], lse [n]).
+ */
+int oracle_sage_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
+                     int layout, int B, int Hq, int Hkv, int Sq, int Sk, int D, double scale,
+                     int causal, int smooth, const int64_t* rows, int64_t n, double* out,
+                     double* lse) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Sq < 0 || Sk < 0 || D <= 0) return -1;
+    const int G = Hq / Hkv;
+    const int64_t nq = ((int64_t)Sq + SAGE_BLOCK - 1) / SAGE_BLOCK;
+    const int64_t nk = ((int64_t)Sk + SAGE_BLOCK - 1) / SAGE_BLOCK;
+    float* kbar = (float*)calloc((size_t)B * Hkv * D + 1, sizeof(float));
+    int8_t* qc = (int8_t*)malloc((size_t)B * Hq * Sq * D + 1);
+    int8_t* kc = (int8_t*)malloc((size_t)B * Hkv * Sk * D + 1);
+    float* qs = (float*)malloc(sizeof(float) * ((size_t)B * Hq * nq + 1));
+    float* ks = (float*)malloc(sizeof(float) * ((size_t)B * Hkv * nk + 1));
+    int err = !kbar || !qc || !kc || !qs || !ks;
+    if (!err && smooth) oracle_sage_kbar(k, dtype, layout, B, Hkv, Sk, D, kbar);
+    if (!err) err = oracle_sage_quant(q, dtype, layout, B, Hq, Sq, D, NULL, qc, qs) != 0;
+    if (!err) err = oracle_sage_quant(k, dtype, layout, B, Hkv, Sk, D, smooth ? kbar : NULL,
+                                      kc, ks) != 0;
+    const int64_t total = rows ? n : (int64_t)B * Hq * Sq;
+    const int64_t kstride = layout == OR_HND ? D : (int64_t)Hkv * D;
+    if (!err) {
+        #pragma omp parallel
+        {
+            double* t = (double*)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
+            if (!t) {
+                #pragma omp atomic write
+                err = 1;
+            } else {
+                #pragma omp for schedule(dynamic, 4)
+                for (int64_t r = 0; r < total; ++r) {
+                    int64_t b, h, i;
+                    if (rows) {
+                        b = rows[3 * r];
+                        h = rows[3 * r + 1];
+                        i = rows[3 * r + 2];
+                        if (b < 0 || b >= B || h < 0 || h >= Hq || i < 0 || i >= Sq) {
+                            #pragma omp atomic write
+                            err = 1;
+                            continue;
+                        }
+                    } else {
+                        b = r / ((int64_t)Hq * Sq);
+                        h = (r / Sq) % Hq;
+                        i = r % Sq;
+                    }
+                    const int64_t g = h / G;
+                    double* o = rows ? out + r * D : out + row_offset(layout, b, h, i, Hq, Sq, D);
+                    double* l = rows ? lse + r : lse + (b * Hq + h) * Sq + i;
+                    for (int d = 0; d < D; ++d) o[d] = 0.0;
+                    const int64_t nv = visible_keys(i, Sq, Sk, causal);
+                    if (nv <= 0) {
+                        *l = -INFINITY;
+                        continue;
+                    }
+                    const int8_t* qi = qc + ((b * Hq + h) * Sq + i) * D;
+                    const double dq = qs[(b * Hq + h) * nq + i / SAGE_BLOCK];
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < nv; ++j) {
+                        const int8_t* kj = kc + ((b * Hkv + g) * Sk + j) * D;
+                        int64_t dot = 0;
+                        for (int d = 0; d < D; ++d) dot += (int64_t)qi[d] * (int64_t)kj[d];
+                        const double dk = ks[(b * Hkv + g) * nk + j / SAGE_BLOCK];
+                        t[j] = scale * dq * dk * (double)dot / M_LN2;
+                        if (t[j] > m) m = t[j];
+                    }
+                    double z = 0.0;
+                    const uint16_t* vb = v + row_offset(layout, b, g, 0, Hkv, Sk, D);
+                    for (int64_t j = 0; j < nv; ++j) {
+                        const double p = exp2(t[j] - m);
+                        z += p;
+                        for (int d = 0; d < D; ++d) o[d] += p * decode(vb[j * kstride + d], dtype);
+                    }
+                    for (int d = 0; d < D; ++d) o[d] /= z;
+                    /* add back scale * q_i . kbar / ln 2 with the unquantised q */
+                    const uint16_t* qraw = q + row_offset(layout, b, h, i, Hq, Sq, D);
+                    double qk = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        qk += decode(qraw[d], dtype) * (double)kbar[(b * Hkv + g) * D + d];
+                    *l = m + log2(z) + scale * qk / M_LN2;
+                }
+            }
+            free(t);
+        }
+    }
+    free(kbar);
+    free(qc);
+    free(kc);
+    free(qs);
+    free(ks);
+    return err ? -1 : 0;
+}
