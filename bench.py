@@ -21,8 +21,10 @@ is timed as well and reported per problem.
 `cpu_baseline` times the fp64 oracle (oracle/, C + OpenMP) on a bounded sample of
 the same workload.  `secondary` reports the other shapes of the same path
 (the decode on a partly filled KV cache bounded by a device kv_len, wide-head
-decode, varlen causal prefill, ring-style chunked prefill, the tiny LSE case) in
-us, GB/s or TFLOP/s and as a fraction of the roofline.
+decode, varlen causal prefill, ring-style chunked prefill, a dense D128 prefill,
+the tiny LSE case) in us, GB/s or TFLOP/s and as a fraction of the roofline, plus
+the INT8 QK^T path (skv_sage_fwd, smoothing on) on the ring and dense problems, its
+fraction taken against the combined int8 + fp16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -41,6 +43,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 / fp16 MFMA, TFLOP/s
+INT8_PEAK_TOPS = 5033.2        # MI355X dense int8 MFMA, TOP/s
+# INT8 QK^T + fp16 P.V: per (query, key) pair 2D int8 ops and 2D fp16 flops, so at both
+# peaks the 4D "attention flops" of a pair take 2D/INT8 + 2D/FP16 seconds
+INT8_FP16_PEAK_TFLOPS = 4.0 / (2.0 / INT8_PEAK_TOPS + 2.0 / MFMA_PEAK_TFLOPS)
 METRIC = "split-KV decode µs & HBM GB/s (%peak); prefill TFLOP/s (%MFMA peak)"
 
 
@@ -364,6 +370,59 @@ def secondary(skv, args, dec):
         tf = fl / (us * 1e-6) / 1e12
         res[name] = dict(us=round(us, 1), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4),
                          flop=fl)
+    # INT8 QK^T with smoothing (fp16 P.V) on the same ring problem: per chunk + merge,
+    # and unsplit.  Each call quantises its own q and chunk (mean(k), codes, scales),
+    # all inside the timed region.
+    wsr = torch.empty(skv.sage_workspace_bytes(1, 16, 16, 8192, 2048, 64, q.dtype, True),
+                      dtype=torch.uint8, device="cuda")
+    wsf = torch.empty(skv.sage_workspace_bytes(1, 16, 16, 8192, 8192, 64, q.dtype, True),
+                      dtype=torch.uint8, device="cuda")
+
+    def ring_int8():
+        for c in range(4):
+            skv.sage_fwd(q, kc[c], vc[c], scale=rc["scale"], smooth_k=True, out=po[c], lse=pl[c],
+                         workspace=wsr)
+        skv.merge_state(po, pl, out=mo, lse=ml)
+
+    def full_int8():
+        skv.sage_fwd(q, kf, vf, scale=rc["scale"], smooth_k=True, out=fo, lse=fl_, workspace=wsf)
+    for name, fn in (("prefill_int8qk_ring_4chunks_smooth_merge_H16_S8192_D64_fp16", ring_int8),
+                     ("prefill_int8qk_full_smooth_H16_S8192_D64_fp16", full_int8)):
+        us = time_graph(capture(fn), reps)
+        tf = fl / (us * 1e-6) / 1e12
+        res[name] = dict(us=round(us, 1), tflops=round(tf, 1),
+                         frac_mfma_int8_fp16=round(tf / INT8_FP16_PEAK_TFLOPS, 4), flop=fl)
+    del q, kc, vc, kf, vf, po, pl, mo, ml, fo, fl_, wsr, wsf
+    torch.cuda.empty_cache()
+
+    # dense non-causal D128 bf16 (the varlen problem's heads at one 8192-token
+    # sequence): 16-bit path and INT8 QK^T path with smoothing
+    log("generating dense D128 problem")
+    p = wl.attn_problem(1, 32, 8, 8192, 8192, 128, seed=7)
+    q, k, v = p.q.cuda(), p.k.cuda(), p.v.cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 32, 8192), dtype=torch.float32, device="cuda")
+    wsd = torch.empty(skv.sage_workspace_bytes(1, 32, 8, 8192, 8192, 128, q.dtype, True),
+                      dtype=torch.uint8, device="cuda")
+
+    def dense16():
+        skv.attn_fwd(q, k, v, scale=p.scale, out=out, lse=lse)
+
+    def dense8():
+        skv.sage_fwd(q, k, v, scale=p.scale, smooth_k=True, out=out, lse=lse, workspace=wsd)
+    fl = 4 * 32 * 8192 * 8192 * 128
+    us = time_graph(capture(dense16), reps)
+    tf = fl / (us * 1e-6) / 1e12
+    res["prefill_dense_H32_Hkv8_S8192_D128_bf16"] = dict(
+        us=round(us, 1), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4), flop=fl)
+    us = time_graph(capture(dense8), reps)
+    tf = fl / (us * 1e-6) / 1e12
+    res["prefill_int8qk_dense_smooth_H32_Hkv8_S8192_D128_bf16"] = dict(
+        us=round(us, 1), tflops=round(tf, 1),
+        frac_mfma_int8_fp16=round(tf / INT8_FP16_PEAK_TFLOPS, 4), flop=fl)
+    del q, k, v, out, lse, wsd
+    torch.cuda.empty_cache()
+
     # tiny LSE case: B1 H4 Sq64 Sk1000 D128 bf16 (launch-bound)
     d = wl.tiny_lse()
     tq, tk, tv = d["q_rows"].cuda(), d["k"].cuda(), d["v"].cuda()

@@ -36,7 +36,8 @@
  *     D = 96) and touches no memory.  A launch failure returns SKV_ELAUNCH.
  *     skv_last_error() then describes the reason.  No C++ exception crosses the ABI.
  *   - GQA: Hq must be a multiple of Hkv; q head h reads kv head h / (Hq / Hkv).
- *   - Supported: D in {64, 128, 256}; q/k/v in bf16 or fp16.
+ *   - Supported: D in {64, 128, 256} (the INT8 calls: 64, 128); q/k/v in bf16 or
+ *     fp16.
  *   - Layouts: SKV_HND = [B, H, S, D], SKV_NHD = [B, S, H, D] [ARK Problem
  *     Description: both tensor_layout values].
  */
@@ -204,14 +205,72 @@ skv_status_t skv_merge_state(int num_parts, int R0, int R1, int R2, int D,
                              void* out, skv_dtype_t out_dtype, const int64_t out_strides[3],
                              float* lse, const int64_t lse_strides[3], void* stream);
 
-/* Workspace bytes skv_attn_fwd / skv_attn_fwd_varlen need: the float32 mean(k)
- * buffer [B_or_nseq, Hkv, D] when smooth_k != 0, else 0. */
+/* Workspace bytes skv_attn_fwd / skv_attn_fwd_varlen need when smooth_k != 0 (else
+ * 0): the float32 mean(k) buffer [B_or_nseq, Hkv, D] padded to 256 bytes, then, when
+ * U = B_or_nseq * Hkv < 512, the fp64 column sums of the S = min(32, ceil(512 / U))
+ * key ranges each (batch | sequence, kv head) is split into: U * S * D * 8 bytes. */
 size_t skv_workspace_bytes(int B_or_nseq, int Hkv, int D, int smooth_k);
 
 /* A split count for the split-KV calls: about one (batch, kv head, chunk) work
  * group per compute unit (256 CUs), two when chunks would exceed 4096 keys at
  * D <= 128, with chunks of at least 256 keys.  Pure host arithmetic; returns >= 1. */
 int skv_pick_num_splits(int B, int Hkv, int rows_per_kv_head, int Lkv, int D);
+
+/*
+ * INT8 QK^T attention with smoothing [ARK task statement and Reproduction Steps,
+ * the apis table: ark.sagev1 and ark.sageattn(kernel="v1_pvhalf"); Problem
+ * Description, second issue: smooth_k on by default, the LSE must still be that of
+ * the unsmoothed logits].  The pages name these variants without spelling out the
+ * quantisation; this library reads it as follows (one fixed scheme):
+ *
+ *   mean(k)  per (batch, kv head) over the call's Sk keys: the exact mean rounded
+ *            once to float32 (accumulated in fp64); zero without smoothing.
+ *   blocks   32 consecutive rows (query rows of q, or keys of k - mean(k) taken in
+ *            float32) per (batch, head), all D columns; the last block may be short.
+ *   codes    for a block with a = max |x|:  delta = a / 127 and
+ *            code = rint(x * (127 / a)) (0 when a = 0), each a correctly rounded
+ *            float32 operation, round half to even, codes in [-127, 127].
+ *
+ * Quantisation only.  Outputs (device memory, written in full, any alignment the
+ * element type needs):
+ *   q_codes  int8 [B, Hq, Sq, D] and k_codes int8 [B, Hkv, Sk, D], HND order
+ *            whatever the input layout;
+ *   q_scale  float32 [B, Hq, ceil(Sq/32)] and k_scale float32 [B, Hkv, ceil(Sk/32)]
+ *            (the deltas);
+ *   kbar     float32 [B, Hkv, D]: mean(k); required when smooth_k != 0, ignored
+ *            (may be NULL) otherwise.
+ * q, k: as skv_attn_fwd (bf16 or fp16, HND or NHD, 16-byte aligned).  D in {64, 128}.
+ */
+skv_status_t skv_sage_quant(const void* q, const void* k, int B, int Hq, int Hkv, int Sq,
+                            int Sk, int D, skv_dtype_t dtype, skv_layout_t layout, int smooth_k,
+                            int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale,
+                            float* kbar, void* stream);
+
+/*
+ * Attention forward on the INT8 logits of skv_sage_quant's scheme, with P.V in
+ * half precision (P and V rounded to fp16, float32 accumulation) [ARK apis table:
+ * kernel "v1_pvhalf"]:
+ *     t_ij = scale * dQ(i) * dK(j) * (q^_i . k^_j)    (exact integer dot product)
+ *     out_i = sum_j softmax_j(t_ij) v_j
+ *     lse_i = log2 sum_j exp(t_ij) + scale * q_i . mean(k) / ln 2
+ * so with smooth_k the LSE refers to the unsmoothed logits [ARK Reproduction Steps
+ * part 3]; it approximates skv_attn_fwd's LSE to the quantisation error.
+ *
+ * Arguments as skv_attn_fwd (q, k, v, out, lse, sizes, dtype, layout, scale,
+ * causal, smooth_k), with D in {64, 128}.  The workspace (device memory, 256-byte
+ * aligned, no initialisation required) holds the codes, scales, mean(k), the per-row
+ * add-back and, for bf16 inputs, an fp16 copy of V: skv_sage_workspace_bytes(...)
+ * bytes.  V values outside the fp16 range overflow to +-inf in that copy.  Grid
+ * limits as skv_attn_fwd (256 query rows per row tile).
+ */
+skv_status_t skv_sage_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int Sq, int Sk, int D, skv_dtype_t dtype,
+                          skv_layout_t layout, float scale, int causal, int smooth_k,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of skv_sage_fwd (0 for empty problems). */
+size_t skv_sage_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                skv_dtype_t dtype, int smooth_k);
 
 /* Static description of a status code. */
 const char* skv_status_str(skv_status_t status);

@@ -10,7 +10,7 @@ fallback: if the library is missing, every call raises.
 Functions (same names as the C entry points without the ``skv_`` prefix):
     attn_fwd, attn_fwd_varlen, attn_splitkv_partial, attn_splitkv_decode,
     merge_state, workspace_bytes, splitkv_workspace_bytes, pick_num_splits,
-    lse_varlen_to_dense
+    lse_varlen_to_dense, sage_quant, sage_fwd, sage_workspace_bytes
 """
 from __future__ import annotations
 
@@ -21,7 +21,8 @@ import torch
 
 __all__ = ["attn_fwd", "attn_fwd_varlen", "attn_splitkv_partial", "attn_splitkv_decode",
            "merge_state", "workspace_bytes", "splitkv_workspace_bytes", "pick_num_splits",
-           "lse_varlen_to_dense", "SkvError", "lib_path"]
+           "lse_varlen_to_dense", "sage_quant", "sage_fwd", "sage_workspace_bytes", "SkvError",
+           "lib_path"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libskv.so")
@@ -71,6 +72,12 @@ def _load():
     lib.skv_workspace_bytes.restype = SZ
     lib.skv_pick_num_splits.argtypes = [I, I, I, I, I]
     lib.skv_pick_num_splits.restype = I
+    lib.skv_sage_quant.argtypes = [P, P, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P]
+    lib.skv_sage_quant.restype = I
+    lib.skv_sage_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P, SZ, P]
+    lib.skv_sage_fwd.restype = I
+    lib.skv_sage_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.skv_sage_workspace_bytes.restype = SZ
     lib.skv_status_str.argtypes = [I]
     lib.skv_status_str.restype = ctypes.c_char_p
     lib.skv_last_error.argtypes = []
@@ -382,3 +389,77 @@ def lse_varlen_to_dense(lse: torch.Tensor, B: int, S: int) -> torch.Tensor:
     if lse.dim() != 2 or lse.shape[1] != B * S:
         raise ValueError(f"expected a varlen LSE [H, {B}*{S}], got {tuple(lse.shape)}")
     return lse.reshape(lse.shape[0], B, S).transpose(0, 1)
+
+
+# ------------------------------------------------------------- INT8 QK^T path
+
+def sage_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, dtype, smooth_k=True) -> int:
+    dt = dtype if isinstance(dtype, int) else _dt(torch.empty(0, dtype=dtype))
+    return int(_load().skv_sage_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, dt, int(bool(smooth_k))))
+
+
+def sage_quant(q, k, layout="HND", smooth_k=True):
+    """Per-block INT8 quantisation of q and of k - mean(k) (skv_sage_quant).
+
+    Returns dict(q_codes int8 [B,Hq,Sq,D], q_scale float32 [B,Hq,ceil(Sq/32)],
+    k_codes int8 [B,Hkv,Sk,D], k_scale float32 [B,Hkv,ceil(Sk/32)], kbar float32
+    [B,Hkv,D] or None); codes are in HND order whatever the input layout.
+    """
+    lib = _load()
+    for n, t in (("q", q), ("k", k)):
+        _need_cuda_contig(n, t)
+    if q.dtype != k.dtype:
+        raise ValueError("q and k must have the same dtype")
+    B, Hq, Hkv, Sq, Sk, D = _dims(q, k, layout)
+    dev = q.device
+    qc = torch.empty((B, Hq, Sq, D), dtype=torch.int8, device=dev)
+    qs = torch.empty((B, Hq, (Sq + 31) // 32), dtype=torch.float32, device=dev)
+    kc = torch.empty((B, Hkv, Sk, D), dtype=torch.int8, device=dev)
+    ks = torch.empty((B, Hkv, (Sk + 31) // 32), dtype=torch.float32, device=dev)
+    kb = torch.empty((B, Hkv, D), dtype=torch.float32, device=dev) if smooth_k else None
+    _check(lib.skv_sage_quant(_ptr(q), _ptr(k), B, Hq, Hkv, Sq, Sk, D, _dt(q),
+                              SKV_HND if layout == "HND" else SKV_NHD, int(bool(smooth_k)),
+                              _ptr(qc), _ptr(qs), _ptr(kc), _ptr(ks), _ptr(kb), _stream(dev)))
+    return dict(q_codes=qc, q_scale=qs, k_codes=kc, k_scale=ks, kbar=kb)
+
+
+def sage_fwd(q, k, v, scale=None, layout="HND", causal=False, smooth_k=True, return_lse=False,
+             out=None, lse=None, workspace=None):
+    """Attention with INT8 QK^T and half-precision P.V (skv_sage_fwd).
+
+    Arguments and results as ``attn_fwd``; smoothing is on by default.  The LSE
+    (float32 [B, Hq, Sq], log2) refers to the unsmoothed logits.  ``workspace``: a
+    uint8 GPU tensor of at least ``sage_workspace_bytes(...)`` bytes, or None to
+    allocate one.
+    """
+    lib = _load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda_contig(n, t)
+    if v.shape != k.shape or v.dtype != k.dtype or q.dtype != k.dtype:
+        raise ValueError("k and v must match in shape, and q, k, v in dtype")
+    B, Hq, Hkv, Sq, Sk, D = _dims(q, k, layout)
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda_contig("out", out)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need_cuda_contig("lse", lse)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq):
+            raise ValueError(f"lse must be float32 {(B, Hq, Sq)}")
+    dt = _dt(q)
+    ws_n = int(lib.skv_sage_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, dt, int(bool(smooth_k))))
+    if workspace is None:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    _need_cuda_contig("workspace", workspace)
+    if workspace.numel() * workspace.element_size() < ws_n:
+        raise ValueError(f"workspace must hold {ws_n} bytes")
+    _check(lib.skv_sage_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk,
+                            D, dt, SKV_HND if layout == "HND" else SKV_NHD, float(scale),
+                            int(bool(causal)), int(bool(smooth_k)), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return (out, lse) if (return_lse or lse is not None) else out

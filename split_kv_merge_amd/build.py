@@ -20,7 +20,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libskv.so")
 INCLUDE = os.path.join(ROOT, "include")
 
-SOURCES = ["api.cpp", "fmha_fwd.hip", "splitkv.hip", "merge.hip", "kmean.hip"]
+SOURCES = ["api.cpp", "fmha_fwd.hip", "splitkv.hip", "merge.hip", "kmean.hip",
+           "sage_quant.hip", "sage_fwd.hip"]
 ARCH = "gfx950"
 
 

@@ -67,6 +67,31 @@ skv_status_t check_heads_dims(int Hq, int Hkv, int D, int dtype) {
     return SKV_OK;
 }
 
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// mean(k) buffer: float32 [units, D], padded to 256 bytes.
+size_t kbar_bytes(size_t units, int D) { return round256(units * (size_t)D * sizeof(float)); }
+
+// fp64 split sums of the mean(k) kernel for the largest split count it may pick
+// for this many (batch | sequence, kv head) units (none when it keeps one split).
+size_t kmean_partial_bytes(size_t units, int D) {
+    const int s = skv::kmean_splits((int64_t)units, INT64_MAX);
+    return s > 1 ? units * (size_t)s * (size_t)D * sizeof(double) : 0;
+}
+
+// Launch the mean(k) kernels into kbar, with split sums in `partial` (which must
+// hold kmean_partial_bytes) or, when partial is null, one split per unit.
+skv_status_t run_kmean_into(const void* k, float* kbar, double* partial, const int32_t* cu_k,
+                            int units_b, int Hkv, int Sk, int64_t keys_per_unit, int D, int dtype,
+                            int64_t kv_row, int64_t kv_head, int64_t kv_batch, hipStream_t s) {
+    skv::KmeanArgs km{};
+    km.k = k; km.kbar = kbar; km.partial = partial; km.cu_k = cu_k;
+    km.Hkv = Hkv; km.Sk = Sk;
+    km.nsplit = partial ? skv::kmean_splits((int64_t)units_b * Hkv, keys_per_unit) : 1;
+    km.kv_row = kv_row; km.kv_head = kv_head; km.kv_batch = kv_batch;
+    return launched(skv::launch_kmean(km, dtype, D, cu_k != nullptr, units_b, s), "kmean");
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,7 +110,8 @@ const char* skv_last_error(void) { return g_err; }
 
 size_t skv_workspace_bytes(int B_or_nseq, int Hkv, int D, int smooth_k) {
     if (!smooth_k || B_or_nseq <= 0 || Hkv <= 0 || D <= 0) return 0;
-    return (size_t)B_or_nseq * (size_t)Hkv * (size_t)D * sizeof(float);
+    const size_t units = (size_t)B_or_nseq * (size_t)Hkv;
+    return kbar_bytes(units, D) + kmean_partial_bytes(units, D);
 }
 
 int skv_pick_num_splits(int B, int Hkv, int rows_per_kv_head, int Lkv, int D) {
@@ -158,10 +184,9 @@ skv_status_t skv_attn_fwd(const void* q, const void* k, const void* v, void* out
     a.lse_batch = (int64_t)Hq * Sq;
     a.scale_log2 = scale * 1.4426950408889634f;
     if (smooth_k) {
-        skv::KmeanArgs km{};
-        km.k = k; km.kbar = (float*)workspace; km.Hkv = Hkv; km.Sk = Sk;
-        km.kv_row = a.kv_row; km.kv_head = a.kv_head; km.kv_batch = a.kv_batch;
-        st = launched(skv::launch_kmean(km, dtype, D, false, B, s), "kmean");
+        char* ws = (char*)workspace;
+        st = run_kmean_into(k, (float*)ws, (double*)(ws + kbar_bytes((size_t)B * Hkv, D)), nullptr,
+                            B, Hkv, Sk, Sk, D, dtype, a.kv_row, a.kv_head, a.kv_batch, s);
         if (st != SKV_OK) return st;
         a.kbar = (const float*)workspace;
     }
@@ -219,10 +244,10 @@ skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
     a.lse_head = total_q; a.lse_batch = 0;
     a.scale_log2 = scale * 1.4426950408889634f;
     if (smooth_k) {
-        skv::KmeanArgs km{};
-        km.k = k; km.kbar = (float*)workspace; km.cu_k = cu_seqlens_k; km.Hkv = Hkv;
-        km.kv_row = a.kv_row; km.kv_head = a.kv_head;
-        st = launched(skv::launch_kmean(km, dtype, D, true, nseq, s), "kmean");
+        char* ws = (char*)workspace;
+        st = run_kmean_into(k, (float*)ws, (double*)(ws + kbar_bytes((size_t)nseq * Hkv, D)),
+                            cu_seqlens_k, nseq, Hkv, 0, total_k / nseq, D, dtype, a.kv_row,
+                            a.kv_head, 0, s);
         if (st != SKV_OK) return st;
         a.kbar = (const float*)workspace;
     }
@@ -383,6 +408,180 @@ skv_status_t skv_merge_state(int num_parts, int R0, int R1, int R2, int D,
     a.o_s0 = out_strides[0]; a.o_s1 = out_strides[1]; a.o_s2 = out_strides[2];
     if (lse) { a.l_s0 = lse_strides[0]; a.l_s1 = lse_strides[1]; a.l_s2 = lse_strides[2]; }
     return launched(skv::launch_merge(a, parts_dtype, out_dtype, D, (hipStream_t)stream), "merge_state");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------- INT8 QK^T (skv_sage_*)
+
+namespace {
+
+// Byte offsets of the INT8 path's buffers inside one workspace, each 256-byte
+// aligned: mean(k), q codes, q scales, q add-back, k codes, k scales, fp16 V.
+struct SageLayout {
+    size_t kbar, part, qc, qs, qb, kc, ks, v16, total;
+};
+
+SageLayout sage_layout(int B, int Hq, int Hkv, int Sq, int Sk, int D, int dtype, int smooth) {
+    SageLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += round256(bytes);
+        return o;
+    };
+    const size_t nq = ((size_t)Sq + 31) / 32, nk = ((size_t)Sk + 31) / 32;
+    L.kbar = take(smooth ? (size_t)B * Hkv * D * 4 : 0);
+    L.part = take(smooth ? kmean_partial_bytes((size_t)B * Hkv, D) : 0);
+    L.qc = take((size_t)B * Hq * Sq * D);
+    L.qs = take((size_t)B * Hq * nq * 4);
+    L.qb = take(smooth ? (size_t)B * Hq * Sq * 4 : 0);
+    L.kc = take((size_t)B * Hkv * Sk * D);
+    L.ks = take((size_t)B * Hkv * nk * 4);
+    L.v16 = take(dtype == SKV_BF16 ? (size_t)B * Hkv * Sk * D * 2 : 0);
+    L.total = off;
+    return L;
+}
+
+// Checks shared by skv_sage_quant and skv_sage_fwd.
+skv_status_t check_sage(const void* q, const void* k, int B, int Hq, int Hkv, int Sq, int Sk,
+                        int D, int dtype, int layout) {
+    if (!q) return fail(SKV_EINVAL, "q must be non-NULL");
+    if (!k && Sk > 0) return fail(SKV_EINVAL, "k must be non-NULL when Sk > 0");
+    if (B < 0 || Sq < 0 || Sk < 0)
+        return fail(SKV_EINVAL, "sizes must be non-negative (B=%d, Sq=%d, Sk=%d)", B, Sq, Sk);
+    skv_status_t st = check_heads_dims(Hq, Hkv, D, dtype);
+    if (st != SKV_OK) return st;
+    if (D != 64 && D != 128)
+        return fail(SKV_EUNSUPPORTED, "the INT8 path is built for D = 64 and 128 (D=%d)", D);
+    if (!valid_layout(layout)) return fail(SKV_EINVAL, "unknown layout code %d", layout);
+    if (!aligned(q, 16) || !aligned(k, 16)) return fail(SKV_EINVAL, "q and k must be 16-byte aligned");
+    if (B > 65535) return fail(SKV_EUNSUPPORTED, "B=%d exceeds the 65535 grid limit", B);
+    if (!elems_ok({B, Hq, Sq, D}) || !elems_ok({B, Hkv, Sk, D}))
+        return fail(SKV_EINVAL, "tensor sizes overflow 64-bit indexing");
+    const int64_t items = (int64_t)B * Hq * ((Sq + 31) / 32) + (int64_t)B * Hkv * ((Sk + 31) / 32);
+    if ((items + 3) / 4 > INT32_MAX)
+        return fail(SKV_EUNSUPPORTED, "%lld quantisation blocks exceed the grid limit", (long long)items);
+    return SKV_OK;
+}
+
+// Quantisation launch arguments for q / k in `layout`.
+skv::SageQuantArgs quant_args(const void* q, const void* k, int B, int Hq, int Hkv, int Sq,
+                              int Sk, int D, int layout) {
+    const bool hnd = layout == SKV_HND;
+    skv::SageQuantArgs a{};
+    a.q = q; a.k = k;
+    a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk;
+    a.q_items = (int64_t)B * Hq * ((Sq + 31) / 32);
+    a.k_items = (int64_t)B * Hkv * ((Sk + 31) / 32);
+    a.x_row[0] = hnd ? D : (int64_t)Hq * D;
+    a.x_head[0] = hnd ? (int64_t)Sq * D : D;
+    a.x_batch[0] = (int64_t)Hq * Sq * D;
+    a.x_row[1] = hnd ? D : (int64_t)Hkv * D;
+    a.x_head[1] = hnd ? (int64_t)Sk * D : D;
+    a.x_batch[1] = (int64_t)Hkv * Sk * D;
+    return a;
+}
+
+skv_status_t run_kmean(const void* k, float* kbar, double* partial, int B, int Hkv, int Sk, int D,
+                       int dtype, const skv::SageQuantArgs& qa, hipStream_t s) {
+    return run_kmean_into(k, kbar, partial, nullptr, B, Hkv, Sk, Sk, D, dtype, qa.x_row[1],
+                          qa.x_head[1], qa.x_batch[1], s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t skv_sage_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                skv_dtype_t dtype, int smooth_k) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk < 0 || D <= 0) return 0;
+    return sage_layout(B, Hq, Hkv, Sq, Sk, D, dtype, smooth_k != 0).total;
+}
+
+skv_status_t skv_sage_quant(const void* q, const void* k, int B, int Hq, int Hkv, int Sq,
+                            int Sk, int D, skv_dtype_t dtype, skv_layout_t layout, int smooth_k,
+                            int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale,
+                            float* kbar, void* stream) {
+    clear_err();
+    skv_status_t st = check_sage(q, k, B, Hq, Hkv, Sq, Sk, D, dtype, layout);
+    if (st != SKV_OK) return st;
+    if (!q_codes || !q_scale || (Sk > 0 && (!k_codes || !k_scale)))
+        return fail(SKV_EINVAL, "q_codes, q_scale, k_codes and k_scale must be non-NULL");
+    if (smooth_k && !kbar) return fail(SKV_EINVAL, "smooth_k needs the kbar output");
+    if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(q_scale, 4) ||
+        !aligned(k_scale, 4) || (kbar && !aligned(kbar, 4)))
+        return fail(SKV_EINVAL, "code buffers must be 16-byte and scale buffers 4-byte aligned");
+    if (B == 0 || (Sq == 0 && Sk == 0)) return SKV_OK;
+    hipStream_t s = (hipStream_t)stream;
+    skv::SageQuantArgs a = quant_args(q, k, B, Hq, Hkv, Sq, Sk, D, layout);
+    a.q_codes = q_codes; a.q_scale = q_scale; a.k_codes = k_codes; a.k_scale = k_scale;
+    if (smooth_k) {
+        st = run_kmean(k, kbar, nullptr, B, Hkv, Sk, D, dtype, a, s);
+        if (st != SKV_OK) return st;
+        a.kbar = kbar;
+    }
+    return launched(skv::launch_sage_quant(a, dtype, D, s), "sage_quant");
+}
+
+skv_status_t skv_sage_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int Sq, int Sk, int D, skv_dtype_t dtype,
+                          skv_layout_t layout, float scale, int causal, int smooth_k,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    clear_err();
+    skv_status_t st = check_sage(q, k, B, Hq, Hkv, Sq, Sk, D, dtype, layout);
+    if (st != SKV_OK) return st;
+    if (!out) return fail(SKV_EINVAL, "out must be non-NULL");
+    if (!v && Sk > 0) return fail(SKV_EINVAL, "v must be non-NULL when Sk > 0");
+    if (!aligned(v, 16) || !aligned(out, 16)) return fail(SKV_EINVAL, "v and out must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(SKV_EINVAL, "lse must be 4-byte aligned");
+    if (!std::isfinite(scale)) return fail(SKV_EINVAL, "scale must be finite");
+    const int grid_m = (int)(((int64_t)Sq + skv::sage_rows_per_block() - 1) / skv::sage_rows_per_block());
+    if (grid_m > 65535)
+        return fail(SKV_EUNSUPPORTED, "Sq=%d needs %d row tiles, over the 65535 grid limit", Sq, grid_m);
+    if (B == 0 || Sq == 0) return SKV_OK;
+    const SageLayout L = sage_layout(B, Hq, Hkv, Sq, Sk, D, dtype, smooth_k != 0);
+    if (!workspace || !aligned(workspace, 256))
+        return fail(SKV_EINVAL, "the INT8 path needs a 256-byte aligned workspace");
+    if (workspace_bytes < L.total)
+        return fail(SKV_EINVAL, "workspace has %zu bytes, the INT8 path needs %zu", workspace_bytes, L.total);
+
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    const float scale_log2 = scale * 1.4426950408889634f;
+    skv::SageQuantArgs a = quant_args(q, k, B, Hq, Hkv, Sq, Sk, D, layout);
+    a.v = v;
+    a.q_codes = (int8_t*)(ws + L.qc);
+    a.q_scale = (float*)(ws + L.qs);
+    a.k_codes = (int8_t*)(ws + L.kc);
+    a.k_scale = (float*)(ws + L.ks);
+    a.scale_log2 = scale_log2;
+    if (dtype == SKV_BF16) a.v16 = (uint16_t*)(ws + L.v16);
+    if (smooth_k) {
+        st = run_kmean(k, (float*)(ws + L.kbar), (double*)(ws + L.part), B, Hkv, Sk, D, dtype, a, s);
+        if (st != SKV_OK) return st;
+        a.kbar = (const float*)(ws + L.kbar);
+        a.q_bias = (float*)(ws + L.qb);
+    }
+    st = launched(skv::launch_sage_quant(a, dtype, D, s), "sage_quant");
+    if (st != SKV_OK) return st;
+
+    const bool hnd = layout == SKV_HND;
+    skv::SageFwdArgs f{};
+    f.q_codes = a.q_codes; f.q_scale = a.q_scale; f.q_bias = a.q_bias;
+    f.k_codes = a.k_codes; f.k_scale = a.k_scale;
+    if (a.v16) {
+        f.v = a.v16;
+        f.v_row = D; f.v_head = (int64_t)Sk * D; f.v_batch = (int64_t)Hkv * Sk * D;
+    } else {
+        f.v = (const uint16_t*)v;
+        f.v_row = a.x_row[1]; f.v_head = a.x_head[1]; f.v_batch = a.x_batch[1];
+    }
+    f.out = out; f.lse = lse;
+    f.Hq = Hq; f.Hkv = Hkv; f.Sq = Sq; f.Sk = Sk;
+    f.o_row = a.x_row[0]; f.o_head = a.x_head[0]; f.o_batch = a.x_batch[0];
+    f.scale_log2 = scale_log2;
+    return launched(skv::launch_sage_fwd(f, dtype, D, causal != 0, grid_m, B, s), "sage_fwd");
 }
 
 }  // extern "C"

@@ -5,7 +5,10 @@
 // subtracts mean(k), taken along the key axis, from every key; the attention
 // kernel turns that into a per-row logit bias and adds it back into the LSE.
 // One work group streams the keys of one (batch, kv head) with 16-byte loads,
-// accumulates in fp32 and reduces through LDS.
+// accumulates in fp64 and reduces through LDS: the sum of 16-bit inputs is then
+// exact whatever the order (their significant bits span far less than 53 bits
+// for any realistic key range), so mean(k) is the exact mean rounded once to
+// float32 -- the value the INT8 path's codes are defined on.
 #include "device.h"
 #include "launch.h"
 
@@ -13,14 +16,18 @@ namespace skv {
 
 namespace {
 
+// Grid (kv head, batch | sequence, split): split s sums keys [s*C, min((s+1)*C, Lk))
+// with C = ceil(Lk / nsplit), so even one (batch, kv head) spreads over many
+// compute units.  With one split the mean is written directly; otherwise each
+// split writes its fp64 column sums and kmean_finish_kernel adds them in order.
 template <typename T, int D, bool VARLEN>
 __global__ __launch_bounds__(256) void kmean_kernel(KmeanArgs a) {
     using E = Elem<T>;
     constexpr int CPR = D / 8;      // threads per key row
     constexpr int RPP = 256 / CPR;  // key rows per pass
-    __shared__ float red[RPP * D];
+    __shared__ double red[RPP * D];
 
-    const int tid = threadIdx.x, g = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, g = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
     int Lk;
     int64_t off;
     if (VARLEN) {
@@ -31,13 +38,16 @@ __global__ __launch_bounds__(256) void kmean_kernel(KmeanArgs a) {
         Lk = a.Sk;
         off = (int64_t)b * a.kv_batch;
     }
+    const int64_t C = ((int64_t)Lk + a.nsplit - 1) / a.nsplit;
+    const int j0 = (int)min((int64_t)sp * C, (int64_t)Lk);
+    const int j1 = (int)min((int64_t)j0 + C, (int64_t)Lk);
     const uint16_t* kp = (const uint16_t*)a.k + off + (int64_t)g * a.kv_head + (tid % CPR) * 8;
 
     // Eight rows in flight per thread: the loop is latency-bound otherwise.
     constexpr int U = 8;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int j = tid / CPR;
-    for (; j + (U - 1) * RPP < Lk; j += U * RPP) {
+    double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    int j = j0 + tid / CPR;
+    for (; j + (U - 1) * RPP < j1; j += U * RPP) {
         u32x4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) v[u] = load16(kp + (int64_t)(j + u * RPP) * a.kv_row);
@@ -49,7 +59,7 @@ __global__ __launch_bounds__(256) void kmean_kernel(KmeanArgs a) {
                 acc[2 * w + 1] += E::to_float((uint16_t)(v[u][w] >> 16));
             }
     }
-    for (; j < Lk; j += RPP) {
+    for (; j < j1; j += RPP) {
         const u32x4 v = load16(kp + (int64_t)j * a.kv_row);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -61,11 +71,32 @@ __global__ __launch_bounds__(256) void kmean_kernel(KmeanArgs a) {
     for (int w = 0; w < 8; ++w) red[(tid / CPR) * D + (tid % CPR) * 8 + w] = acc[w];
     __syncthreads();
     if (tid < D) {
-        float sum = 0.f;
+        double sum = 0.0;
 #pragma unroll
         for (int r = 0; r < RPP; ++r) sum += red[r * D + tid];
-        a.kbar[((int64_t)b * a.Hkv + g) * D + tid] = Lk > 0 ? sum / (float)Lk : 0.f;
+        const int64_t bg = (int64_t)b * a.Hkv + g;
+        if (a.nsplit == 1)
+            a.kbar[bg * D + tid] = Lk > 0 ? (float)(sum / (double)Lk) : 0.f;
+        else
+            a.partial[(bg * a.nsplit + sp) * D + tid] = sum;
     }
+}
+
+// mean = (sum of the split sums, in split order) / Lk, rounded once to float32.
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(D) void kmean_finish_kernel(KmeanArgs a) {
+    const int g = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int Lk = VARLEN ? a.cu_k[b + 1] - a.cu_k[b] : a.Sk;
+    const int64_t bg = (int64_t)b * a.Hkv + g;
+    // all loads first (independent), then the sum in split order
+    double part[kMaxKmeanSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxKmeanSplits; ++sp)
+        part[sp] = sp < a.nsplit ? a.partial[(bg * a.nsplit + sp) * D + d] : 0.0;
+    double sum = 0.0;
+#pragma unroll
+    for (int sp = 0; sp < kMaxKmeanSplits; ++sp) sum += part[sp];
+    a.kbar[bg * D + d] = Lk > 0 ? (float)(sum / (double)Lk) : 0.f;
 }
 
 template <typename T, int D>
@@ -74,6 +105,13 @@ hipError_t launch_kmean_t(const KmeanArgs& a, bool varlen, dim3 grid, hipStream_
         hipLaunchKernelGGL((kmean_kernel<T, D, true>), grid, dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL((kmean_kernel<T, D, false>), grid, dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    const dim3 g2(grid.x, grid.y);
+    if (varlen)
+        hipLaunchKernelGGL((kmean_finish_kernel<D, true>), g2, dim3(D), 0, st, a);
+    else
+        hipLaunchKernelGGL((kmean_finish_kernel<D, false>), g2, dim3(D), 0, st, a);
     return hipGetLastError();
 }
 
@@ -89,9 +127,20 @@ hipError_t launch_kmean_d(const KmeanArgs& a, int D, bool varlen, dim3 grid, hip
 
 }  // namespace
 
+// About two work groups per compute unit over the whole launch, each with at least
+// 128 keys, at most kMaxKmeanSplits per (batch, kv head).
+int kmean_splits(int64_t units, int64_t keys_per_unit) {
+    if (units <= 0) return 1;
+    int64_t s = (512 + units - 1) / units;
+    const int64_t by_len = keys_per_unit / 128 + (keys_per_unit % 128 != 0);
+    if (s > by_len) s = by_len;
+    if (s > kMaxKmeanSplits) s = kMaxKmeanSplits;
+    return s < 1 ? 1 : (int)s;
+}
+
 hipError_t launch_kmean(const KmeanArgs& a, int dtype, int D, bool varlen, int grid_b,
                         hipStream_t stream) {
-    const dim3 grid((unsigned)a.Hkv, (unsigned)grid_b);
+    const dim3 grid((unsigned)a.Hkv, (unsigned)grid_b, (unsigned)a.nsplit);
     if (dtype == 0) return launch_kmean_d<__bf16>(a, D, varlen, grid, stream);
     return launch_kmean_d<_Float16>(a, D, varlen, grid, stream);
 }

@@ -25,14 +25,20 @@ struct FmhaArgs {
     float scale_log2;           // scale * log2(e)
 };
 
-// mean(k) over keys per (batch | sequence, kv head): float32 [B | nseq, Hkv, D]
+// mean(k) over keys per (batch | sequence, kv head): float32 [B | nseq, Hkv, D].
+// nsplit > 1 spreads each (batch, kv head) over nsplit work groups, whose fp64
+// column sums go to partial [B | nseq, Hkv, nsplit, D] before a second kernel adds
+// them; nsplit == 1 needs no partial buffer.
+constexpr int kMaxKmeanSplits = 32;
 struct KmeanArgs {
     const void* k;
     float* kbar;
+    double* partial;
     const int32_t* cu_k;        // varlen only
-    int Hkv, Sk;
+    int Hkv, Sk, nsplit;
     int64_t kv_row, kv_head, kv_batch;
 };
+int kmean_splits(int64_t units, int64_t keys_per_unit);  // nsplit for a launch
 
 // Split-KV partial states.
 struct SplitArgs {
@@ -70,6 +76,45 @@ struct MergeArgs {
     int64_t l_s0, l_s1, l_s2;
 };
 
+// INT8 quantisation of q and of k - mean(k) (sage_quant.hip).  Strides in elements:
+// index 0 is q's, index 1 is k's (and v's).
+struct SageQuantArgs {
+    const void* q;
+    const void* k;
+    const void* v;              // read only when v16 is set
+    const float* kbar;          // [B, Hkv, D] or null (no smoothing)
+    int8_t* q_codes;            // [B, Hq, Sq, D]
+    float* q_scale;             // [B, Hq, ceil(Sq/32)]
+    float* q_bias;              // [B, Hq, Sq] add-back in log2 units, or null
+    int8_t* k_codes;            // [B, Hkv, Sk, D]
+    float* k_scale;             // [B, Hkv, ceil(Sk/32)]
+    uint16_t* v16;              // [B, Hkv, Sk, D] fp16 copy of v, or null
+    int Hq, Hkv, Sq, Sk;
+    int64_t q_items, k_items;   // 32-row blocks of q and of k
+    int64_t x_row[2], x_head[2], x_batch[2];
+    float scale_log2;
+};
+
+// INT8 QK^T attention (sage_fwd.hip) on the buffers above.
+struct SageFwdArgs {
+    const int8_t* q_codes;
+    const float* q_scale;
+    const float* q_bias;        // nullable
+    const int8_t* k_codes;
+    const float* k_scale;
+    const uint16_t* v;          // fp16
+    void* out;                  // q's dtype
+    float* lse;                 // [B, Hq, Sq] or null
+    int Hq, Hkv, Sq, Sk;
+    int64_t v_row, v_head, v_batch;
+    int64_t o_row, o_head, o_batch;
+    float scale_log2;
+};
+
+int sage_rows_per_block();     // query rows of one INT8 attention work group
+hipError_t launch_sage_quant(const SageQuantArgs& a, int dtype, int D, hipStream_t stream);
+hipError_t launch_sage_fwd(const SageFwdArgs& a, int dtype, int D, bool causal, int grid_m,
+                           int grid_b, hipStream_t stream);
 int fmha_rows_per_block(int D);  // query rows one attention work group covers
 hipError_t launch_fmha(const FmhaArgs& a, int dtype, int D, bool causal, bool varlen,
                        int grid_m, int grid_b, hipStream_t stream);

@@ -1,0 +1,149 @@
+// sage_quant.hip -- per-block INT8 quantisation of Q and smoothed K for the
+// INT8 QK^T attention path.
+//
+// The ARK return_lse report (auto-round #2556; task statement and Reproduction
+// Steps, the apis table) names INT8 variants ark.sagev1 and
+// ark.sageattn(kernel="v1_pvhalf"), with smooth_k on by default (Problem
+// Description, second issue).  The quantisation follows the plainest reading of
+// such an INT8 QK^T: per (batch, head), blocks of 32 consecutive rows (query rows
+// or keys) over all D columns; for a block with a = max |x|,
+//     delta = a / 127,  iota = a > 0 ? 127 / a : 0,  code = rint(x * iota),
+// each a single correctly rounded float32 operation (round half to even), where
+// x = q for queries and x = k - mean(k) (float32 subtraction) for keys when
+// smoothing.  One wave owns one block: its lanes hold the block's D-wide rows in
+// 16-byte column chunks, the absmax is a wave reduction, and codes are written 8
+// bytes per chunk.  The same pass also writes, per query row, the smoothing
+// add-back c * (q . mean(k)) (c = scale * log2 e) that the LSE epilogue needs,
+// and, for bf16 inputs, the fp16 copy of V that the half-precision P.V reads.
+#include "device.h"
+#include "launch.h"
+
+namespace skv {
+
+namespace {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void sage_quant_kernel(SageQuantArgs a) {
+    using E = Elem<T>;
+    constexpr int CPR = D / 8;        // 16-byte chunks per row
+    constexpr int RPP = 64 / CPR;     // rows per pass of one wave
+    constexpr int NP = 32 / RPP;      // passes per 32-row block
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // one block per wave
+    const int chunk = lane % CPR, rsub = lane / CPR;
+
+    const bool is_q = item < a.q_items;
+    const int64_t it = is_q ? item : item - a.q_items;
+    if (!is_q && it >= a.k_items) return;  // uniform per wave
+    const int H = is_q ? a.Hq : a.Hkv;
+    const int S = is_q ? a.Sq : a.Sk;
+    const int nblk = (S + 31) / 32;
+    const int blk = (int)(it % nblk);
+    const int64_t bh = it / nblk;     // b * H + h
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const int g = is_q ? h / (a.Hq / a.Hkv) : h;
+    const uint16_t* src = (const uint16_t*)(is_q ? a.q : a.k) + (int64_t)b * a.x_batch[is_q ? 0 : 1] +
+                          (int64_t)h * a.x_head[is_q ? 0 : 1];
+    const int64_t xrow = a.x_row[is_q ? 0 : 1];
+
+    // mean(k) of this chunk's 8 columns (the kv head of this q head for the add-back)
+    float kb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        kb[e] = a.kbar ? a.kbar[((int64_t)b * a.Hkv + g) * D + chunk * 8 + e] : 0.f;
+
+    float x[NP][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int row = blk * 32 + p * RPP + rsub;
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (row < S) raw = load16(src + (int64_t)row * xrow + chunk * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            x[p][2 * w] = E::to_float((uint16_t)(raw[w] & 0xffff));
+            x[p][2 * w + 1] = E::to_float((uint16_t)(raw[w] >> 16));
+        }
+        if (!is_q && row < S) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[p][e] = x[p][e] - kb[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[p][e]));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, xor_shfl(amax, m));
+    // IEEE division (correctly rounded in HIP unless fast-math is asked for)
+    const float delta = amax / 127.f;
+    const float iota = amax > 0.f ? 127.f / amax : 0.f;
+
+    int8_t* codes = (is_q ? a.q_codes : a.k_codes) + (bh * S) * D;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int row = blk * 32 + p * RPP + rsub;
+        if (row >= S) continue;
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float c = __builtin_rintf(x[p][e] * iota);
+            c = fminf(fmaxf(c, -127.f), 127.f);
+            w[e >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (e & 3));
+        }
+        *reinterpret_cast<u32x2*>(codes + (int64_t)row * D + chunk * 8) = u32x2{w[0], w[1]};
+    }
+    if (lane == 0) (is_q ? a.q_scale : a.k_scale)[bh * nblk + blk] = delta;
+
+    if (is_q) {
+        // add-back c * (q_row . mean(k)) from the unquantised q, one value per row
+        if (a.q_bias) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int row = blk * 32 + p * RPP + rsub;
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf(x[p][e], kb[e], acc);
+#pragma unroll
+                for (int m = CPR / 2; m >= 1; m >>= 1) acc += xor_shfl(acc, m);
+                if (chunk == 0 && row < S) a.q_bias[bh * S + row] = acc * a.scale_log2;
+            }
+        }
+    } else if (a.v16) {
+        // fp16 copy of the same rows of V (bf16 inputs only)
+        const uint16_t* vs = (const uint16_t*)a.v + (int64_t)b * a.x_batch[1] + (int64_t)h * a.x_head[1];
+        uint16_t* vd = a.v16 + (bh * S) * D;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int row = blk * 32 + p * RPP + rsub;
+            if (row >= S) continue;
+            const u32x4 raw = load16(vs + (int64_t)row * xrow + chunk * 8);
+            u32x4 o;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                o[w] = Elem<_Float16>::pack2(E::to_float((uint16_t)(raw[w] & 0xffff)),
+                                             E::to_float((uint16_t)(raw[w] >> 16)));
+            store16(vd + (int64_t)row * D + chunk * 8, o);
+        }
+    }
+}
+
+template <typename T>
+hipError_t launch_sage_quant_t(const SageQuantArgs& a, int D, hipStream_t st) {
+    const int64_t items = a.q_items + a.k_items;
+    const dim3 grid((unsigned)((items + 3) / 4));
+    switch (D) {
+        case 64: hipLaunchKernelGGL((sage_quant_kernel<T, 64>), grid, dim3(256), 0, st, a); break;
+        case 128: hipLaunchKernelGGL((sage_quant_kernel<T, 128>), grid, dim3(256), 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sage_quant(const SageQuantArgs& a, int dtype, int D, hipStream_t stream) {
+    if (a.q_items + a.k_items == 0) return hipSuccess;
+    if (dtype == 0) return launch_sage_quant_t<__bf16>(a, D, stream);
+    return launch_sage_quant_t<_Float16>(a, D, stream);
+}
+
+}  // namespace skv

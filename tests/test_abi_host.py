@@ -52,7 +52,10 @@ def test_status_strings(lib):
 
 
 def test_workspace_and_split_heuristic(lib):
-    assert lib.skv_workspace_bytes(2, 8, 128, 1) == 2 * 8 * 128 * 4
+    # mean(k) [B, Hkv, D] float32, then fp64 sums of min(32, ceil(512 / (B*Hkv))) splits
+    assert lib.skv_workspace_bytes(2, 8, 128, 1) == 2 * 8 * 128 * 4 + 2 * 8 * 32 * 128 * 8
+    assert lib.skv_workspace_bytes(16, 8, 64, 1) == 16 * 8 * 64 * 4 + 16 * 8 * 4 * 64 * 8
+    assert lib.skv_workspace_bytes(64, 8, 128, 1) == 64 * 8 * 128 * 4      # one split
     assert lib.skv_workspace_bytes(2, 8, 128, 0) == 0
     for B, Hkv, Lkv in [(8, 8, 4096), (8, 8, 32768), (4, 4, 16384), (1, 1, 10), (1, 2, 0)]:
         s = lib.skv_pick_num_splits(B, Hkv, 4, Lkv, 128)
