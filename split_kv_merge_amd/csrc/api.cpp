@@ -325,7 +325,7 @@ skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* 
 size_t skv_splitkv_workspace_bytes(int B, int Hq, int Lq, int D, int num_splits, int Hkv) {
     if (B <= 0 || Hq <= 0 || Lq <= 0 || D <= 0 || num_splits <= 0 || Hkv <= 0) return 0;
     const size_t rows = (size_t)num_splits * B * Hq * Lq;
-    return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float)) +
+    return align256(rows * D * sizeof(uint16_t)) + align256(rows * sizeof(float)) +
            align256((size_t)B * Hkv * sizeof(int));
 }
 
@@ -354,10 +354,12 @@ skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v
     const size_t rows = (size_t)num_splits * B * Hq * Lq;
     if (rows * D * sizeof(float) >= ((size_t)1 << 31))
         return fail(SKV_EUNSUPPORTED, "partial states exceed 2 GiB for the single-launch decode");
+    // chunk outputs in q's 16-bit type, chunk LSEs float32, one ticket per (batch, kv head)
     char* ws = (char*)workspace;
+    const size_t po_bytes = align256(rows * D * sizeof(uint16_t));
     a.out_part = (float*)ws;
-    a.lse_part = (float*)(ws + align256(rows * D * sizeof(float)));
-    a.ticket = (int*)(ws + align256(rows * D * sizeof(float)) + align256(rows * sizeof(float)));
+    a.lse_part = (float*)(ws + po_bytes);
+    a.ticket = (int*)(ws + po_bytes + align256(rows * sizeof(float)));
     a.out = out;
     a.lse = lse;
     return launched(skv::launch_splitkv(a, dtype, D, true, (hipStream_t)stream), "splitkv_decode");

@@ -45,7 +45,7 @@ struct SplitArgs {
     const void* q;
     const void* k;
     const void* v;
-    float* out_part;
+    float* out_part;            // float32; the single-launch decode keeps q's 16-bit type
     float* lse_part;
     int B, Hq, Hkv, Lq, Lkv, num_splits;
     // filled KV length per batch element (device, nullable: NULL = Lkv for all);

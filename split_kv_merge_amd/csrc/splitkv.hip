@@ -48,6 +48,9 @@ constexpr int kCoherentLoad = 0x10;
 __device__ __forceinline__ void store_agent(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Single-launch decode: once a work group has written its chunk's partial state
 // (with store_agent) it waits for those stores to complete and takes a ticket for
@@ -55,18 +58,23 @@ __device__ __forceinline__ void store_agent(float* p, float v) {
 // all partial states of those rows, writes the output and its LSE, and returns the
 // ticket counter to zero for the next call.
 //
-// The merge keeps memory latency off serial chains: each thread owns Q adjacent
-// 4-column groups of one row and reads the partial LSEs and outputs of eight
-// chunks per round trip, all issued together.  Across groups of eight it keeps a
-// running max M of the chunk LSEs and rescales its sums by 2^(M_old - M_new) when M
-// grows; the result is the stable merge -- out = sum_s 2^(lse_s - M) o_s / sum_s
-// 2^(lse_s - M), lse = M + log2 of that sum -- with no exponent above 0.  Chunks
-// with lse = -inf get weight 0; if every chunk is -inf the row gets (0, -inf).
+// The chunk outputs of this path are published in the input's 16-bit type (each is
+// normalised by its own sum, so it lies in the range of V and the 16-bit type
+// holds it; the merge adds them in fp32), half the bytes the merging work group
+// has to pull in.  The merge keeps memory latency off serial chains: each thread
+// owns Q adjacent 4-column groups of one row and reads the partial LSEs and outputs
+// of GS chunks per round trip (4, 8 or 16: the smallest that covers the split
+// count, up to 16), all issued together.  Across groups of GS it keeps a running max
+// M of the chunk LSEs and rescales its sums by
+// 2^(M_old - M_new) when M grows; the result is the stable merge -- out =
+// sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), lse = M + log2 of that sum -- with
+// no exponent above 0.  Chunks with lse = -inf get weight 0; if every chunk is
+// -inf the row gets (0, -inf).
+template <typename T, int D, int GS>
+__device__ __forceinline__ void merge_rows(const SplitArgs& a, int b, int hk, int R, int G);
+
 template <typename T, int D>
 __device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, int R, int G) {
-    using E = Elem<T>;
-    constexpr int Q = D / 64;          // 4-column groups per thread: 16 rows x D/4 / 256
-    constexpr int GS = 8;              // chunks per round trip
     __shared__ int is_last;
     const int tid = threadIdx.x, S = a.num_splits;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores are done
@@ -78,6 +86,19 @@ __device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, in
     __syncthreads();
     if (!is_last) return;
     if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (S <= 4)
+        merge_rows<T, D, 4>(a, b, hk, R, G);
+    else if (S <= 8)
+        merge_rows<T, D, 8>(a, b, hk, R, G);
+    else
+        merge_rows<T, D, 16>(a, b, hk, R, G);
+}
+
+template <typename T, int D, int GS>
+__device__ __forceinline__ void merge_rows(const SplitArgs& a, int b, int hk, int R, int G) {
+    using E = Elem<T>;
+    constexpr int Q = D / 64;          // 4-column groups per thread: 16 rows x D/4 / 256
+    const int tid = threadIdx.x, S = a.num_splits;
     const int r = tid * Q / (D / 4);   // the row this thread merges
     if (r >= R) return;
     const int d0 = (tid * Q % (D / 4)) * 4;
@@ -99,7 +120,7 @@ __device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, in
     for (int q = 0; q < Q; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += GS) {
         float l[GS];
-        f32x4 x[GS][Q];
+        u32x2 x[GS][Q];
 #pragma unroll
         for (int u = 0; u < GS; ++u) {
             const int sp = min(s0 + u, S - 1);   // past S: a real chunk, weighted 0 below
@@ -107,8 +128,8 @@ __device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, in
                 pl_rsrc, (int)((sp * lse_split + lse_row) * 4), 0, kCoherentLoad));
 #pragma unroll
             for (int q = 0; q < Q; ++q)
-                x[u][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                    po_rsrc, (int)((row_off + d0 + 4 * q + sp * a.part_stride) * 4), 0,
+                x[u][q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                    po_rsrc, (int)((row_off + d0 + 4 * q + sp * a.part_stride) * 2), 0,
                     kCoherentLoad));
         }
         float mg = -INFINITY;
@@ -128,7 +149,13 @@ __device__ __forceinline__ void merge_tail(const SplitArgs& a, int b, int hk, in
             const float w = fast_exp2(l[u] - Mn);   // -inf chunks: 0
             W += w;
 #pragma unroll
-            for (int q = 0; q < Q; ++q) acc[q] += x[u][q] * w;
+            for (int q = 0; q < Q; ++q) {
+                const f32x4 xv = {E::to_float((uint16_t)(x[u][q].x & 0xffff)),
+                                  E::to_float((uint16_t)(x[u][q].x >> 16)),
+                                  E::to_float((uint16_t)(x[u][q].y & 0xffff)),
+                                  E::to_float((uint16_t)(x[u][q].y >> 16))};
+                acc[q] += xv * w;
+            }
         }
         M = Mn;
     }
@@ -343,16 +370,18 @@ void splitkv_kernel(SplitArgs a) {
         }
         const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
         const int h = hk * G + r / a.Lq, i = r % a.Lq;
-        float* op = a.out_part + (int64_t)s * a.part_stride + (int64_t)b * a.q_batch +
-                    (int64_t)h * a.q_head + (int64_t)i * a.q_row + d;
+        const int64_t po = (int64_t)s * a.part_stride + (int64_t)b * a.q_batch +
+                           (int64_t)h * a.q_head + (int64_t)i * a.q_row + d;
         float* lp = a.lse_part + (((int64_t)s * a.B + b) * a.Hq + h) * a.Lq + i;
         const float lse_s = Ls > 0.f ? M + fast_log2(Ls) : -INFINITY;
         if constexpr (FUSED) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) store_agent(op + c, acc[c] * inv);
+            // 16-bit chunk output (workspace), published with one 8-byte store
+            const uint64_t w = (uint64_t)E::pack2(acc[0] * inv, acc[1] * inv) |
+                               ((uint64_t)E::pack2(acc[2] * inv, acc[3] * inv) << 32);
+            store_agent(reinterpret_cast<uint64_t*>((uint16_t*)a.out_part + po), w);
             if (d == 0) store_agent(lp, lse_s);
         } else {
-            *reinterpret_cast<f32x4*>(op) = acc * inv;
+            *reinterpret_cast<f32x4*>(a.out_part + po) = acc * inv;
             if (d == 0) *lp = lse_s;
         }
     }

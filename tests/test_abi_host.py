@@ -204,4 +204,5 @@ def test_splitkv_decode_rejects(lib):
     assert call(B=0) == 0
     need = lib.skv_splitkv_workspace_bytes(2, 32, 1, 128, 8, 8)
     rows = 8 * 2 * 32
-    assert need == ((rows * 128 * 4 + 255) // 256 + (rows * 4 + 255) // 256 + 1) * 256
+    # 16-bit chunk outputs, float32 chunk LSEs, one int32 ticket per (batch, kv head)
+    assert need == ((rows * 128 * 2 + 255) // 256 + (rows * 4 + 255) // 256 + 1) * 256
