@@ -153,3 +153,40 @@ def test_ring_chunk_shape_full_size(skv):
                               smooth_k=True, rows=rows)
     assert_lse_close(np.array([l[b, h, i] for b, h, i in rows]), rl)
     assert_out_close(np.stack([o[b, h, i] for b, h, i in rows]), ro)
+
+
+def test_sage_fwd_graph_replays(skv):
+    """One captured INT8 forward (mean(k), quantisation and attention; no memset in
+    the graph), replayed while q and k change on the device between replays: each
+    replay matches the oracle on the inputs of that moment."""
+    B, Hq, Hkv, Sq, Sk, D = 1, 8, 2, 300, 500, 128
+    q = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=DEV)
+    k = torch.empty((B, Hkv, Sk, D), dtype=torch.bfloat16, device=DEV)
+    v = torch.empty_like(k)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+    ws = torch.empty(skv.sage_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, q.dtype, True),
+                     dtype=torch.uint8, device=DEV)
+    scale = wl.default_scale(D)
+    fn = lambda: skv.sage_fwd(q, k, v, scale=scale, causal=True, smooth_k=True, out=out, lse=lse,
+                              workspace=ws)
+    p0 = wl.attn_problem(B, Hq, Hkv, Sq, Sk, D, seed=40, k_offset=1.0)
+    q.copy_(p0.q), k.copy_(p0.k), v.copy_(p0.v)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        fn()
+    torch.cuda.current_stream().wait_stream(st)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for seed, off in ((41, 0.0), (42, -2.0), (43, 3.0)):
+        p = wl.attn_problem(B, Hq, Hkv, Sq, Sk, D, seed=seed, k_offset=off)
+        q.copy_(p.q), k.copy_(p.k), v.copy_(p.v)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ro, rl = oracle.sage_attn(wl.bits(p.q), wl.bits(p.k), wl.bits(p.v), "bf16", scale=scale,
+                                  causal=True, smooth_k=True)
+        assert_lse_close(lse.cpu().numpy(), rl, f"lse, replay with seed {seed}")
+        assert_out_close(out.float().cpu().numpy(), ro, f"out, replay with seed {seed}")
