@@ -75,7 +75,7 @@ size_t kbar_bytes(size_t units, int D) { return round256(units * (size_t)D * siz
 // fp64 split sums of the mean(k) kernel for the largest split count it may pick
 // for this many (batch | sequence, kv head) units (none when it keeps one split).
 size_t kmean_partial_bytes(size_t units, int D) {
-    const int s = skv::kmean_splits((int64_t)units, INT64_MAX);
+    const int s = skv::kmean_splits((int64_t)units, INT64_MAX / 1024, D);
     return s > 1 ? units * (size_t)s * (size_t)D * sizeof(double) : 0;
 }
 
@@ -87,7 +87,7 @@ skv_status_t run_kmean_into(const void* k, float* kbar, double* partial, const i
     skv::KmeanArgs km{};
     km.k = k; km.kbar = kbar; km.partial = partial; km.cu_k = cu_k;
     km.Hkv = Hkv; km.Sk = Sk;
-    km.nsplit = partial ? skv::kmean_splits((int64_t)units_b * Hkv, keys_per_unit) : 1;
+    km.nsplit = partial ? skv::kmean_splits((int64_t)units_b * Hkv, keys_per_unit, D) : 1;
     km.kv_row = kv_row; km.kv_head = kv_head; km.kv_batch = kv_batch;
     return launched(skv::launch_kmean(km, dtype, D, cu_k != nullptr, units_b, s), "kmean");
 }

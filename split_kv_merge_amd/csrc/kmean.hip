@@ -43,8 +43,9 @@ __global__ __launch_bounds__(256) void kmean_kernel(KmeanArgs a) {
     const int j1 = (int)min((int64_t)j0 + C, (int64_t)Lk);
     const uint16_t* kp = (const uint16_t*)a.k + off + (int64_t)g * a.kv_head + (tid % CPR) * 8;
 
-    // Eight rows in flight per thread: the loop is latency-bound otherwise.
-    constexpr int U = 8;
+    // Sixteen rows in flight per thread (64 KB per work group): with one work group
+    // per (batch, kv head) the loop is latency-bound otherwise.
+    constexpr int U = 16;
     double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     int j = j0 + tid / CPR;
     for (; j + (U - 1) * RPP < j1; j += U * RPP) {
@@ -127,10 +128,13 @@ hipError_t launch_kmean_d(const KmeanArgs& a, int D, bool varlen, dim3 grid, hip
 
 }  // namespace
 
-// About two work groups per compute unit over the whole launch, each with at least
-// 128 keys, at most kMaxKmeanSplits per (batch, kv head).
-int kmean_splits(int64_t units, int64_t keys_per_unit) {
+// One work group per (batch, kv head) while its keys fit in 512 KB (a split costs a
+// second launch, ~4 us); beyond that about two work groups per compute unit over
+// the whole launch, each with at least 128 keys, at most kMaxKmeanSplits per
+// (batch, kv head).
+int kmean_splits(int64_t units, int64_t keys_per_unit, int D) {
     if (units <= 0) return 1;
+    if (keys_per_unit * D * 2 <= (int64_t)512 * 1024) return 1;
     int64_t s = (512 + units - 1) / units;
     const int64_t by_len = keys_per_unit / 128 + (keys_per_unit % 128 != 0);
     if (s > by_len) s = by_len;

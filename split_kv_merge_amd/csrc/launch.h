@@ -38,7 +38,7 @@ struct KmeanArgs {
     int Hkv, Sk, nsplit;
     int64_t kv_row, kv_head, kv_batch;
 };
-int kmean_splits(int64_t units, int64_t keys_per_unit);  // nsplit for a launch
+int kmean_splits(int64_t units, int64_t keys_per_unit, int D);  // nsplit for a launch
 
 // Split-KV partial states.
 struct SplitArgs {

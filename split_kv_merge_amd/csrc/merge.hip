@@ -4,13 +4,14 @@
 // lse = M + log2 sum_s w_s; a part with lse_s = -inf weighs 0 and an all -inf
 // row yields (0, -inf).  This is the global-max rescale of ExecuTorch PR #22133
 // "Prevent Voxtral NaNs in CUDA split-K attention" (Copilot overview), laid out
-// as that PR's reviewer asked for (item 2): the max is a separate, parallel pass
-// and the weighted sum is spread over the head dimension, so no exponential sits
-// on a loop-carried chain.
+// as that PR's reviewer asked for (item 2): the work is spread over the head
+// dimension and over part-groups, and the exponentials of a group of parts are
+// independent of each other rather than one loop-carried chain.
 //
 // Layout: a part-group of D/VEC lanes covers one row's head dimension, each lane
 // owning VEC contiguous elements (one 16-byte load per part); several part-groups
-// share a row so that the parts of one row are read in parallel.
+// share a row so that the parts of one row are read in parallel.  The max is kept
+// as a running max (below), which gives the same result as taking it first.
 #include "device.h"
 #include "launch.h"
 
@@ -75,105 +76,108 @@ template <typename TO, int VEC> struct OutStore {
 
 // A row's parts are split over P part-groups of LPR = D/VEC lanes each; T = P * LPR
 // lanes serve one row (a power of two, at most 256), 256 / T rows per block.
-//   1. max: the row's lanes load the partial LSEs in parallel (lane t takes parts
-//      t, t + T, ...), reduce with xor shuffles inside the wave and, when a row
-//      spans several waves, through LDS;
-//   2. lane (pg, sub) accumulates w_s * o_s over parts s = pg, pg + P, ... for its
-//      VEC elements, w_s = 2^(lse_s - M);
-//   3. the P partial sums of a row are added through LDS by part-group 0.
+//   1. lane (pg, sub) runs an online merge over parts s = pg, pg + P, ... for its VEC
+//      elements, four parts per memory round trip (their LSEs and outputs issued
+//      together): it keeps a running max m of the LSEs it has seen, and when a group
+//      raises it rescales its sums by 2^(m_old - m_new), so every weight
+//      2^(lse_s - m) is at most 1 and no separate max pass (a second round trip) is
+//      needed;
+//   2. part-group 0 combines the P groups' (m_g, W_g, acc_g) through LDS, rescaling
+//      each by 2^(m_g - M) with M the row max.
 template <typename TP, typename TO, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int P) {
     constexpr int VEC = PartLoad<TP>::VEC;
     constexpr int LPR = D / VEC;  // lanes per part-group
-    __shared__ __attribute__((aligned(16))) float red[256 * (VEC + 1)];
-    __shared__ float wmax[4];
+    constexpr int RS = VEC + 2;   // LDS record per lane: acc, W, m
+    __shared__ __attribute__((aligned(16))) float red[256 * RS];
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int T = LPR * P;        // lanes per row
     const int rib = tid / T, t = tid % T, pg = t / LPR, sub = t % LPR;
     const int64_t row = (int64_t)blockIdx.x * (256 / T) + rib;
     const bool live = row < a.rows;
 
+    // (r0, r1, r2) of this row; 32-bit division whenever the row count allows it (a
+    // 64-bit division is a long software sequence, and every lane does three)
     int64_t r0 = 0, r1 = 0, r2 = 0;
     if (live) {
-        r2 = row % a.R2;
-        r1 = (row / a.R2) % a.R1;
-        r0 = row / ((int64_t)a.R1 * a.R2);
+        if (a.rows <= 0xffffffffll) {
+            const uint32_t rw = (uint32_t)row, R2 = (uint32_t)a.R2, R1 = (uint32_t)a.R1;
+            const uint32_t q2 = rw / R2;
+            r2 = rw - q2 * R2;
+            r1 = q2 % R1;
+            r0 = q2 / R1;
+        } else {
+            r2 = row % a.R2;
+            r1 = (row / a.R2) % a.R1;
+            r0 = row / ((int64_t)a.R1 * a.R2);
+        }
     }
     const float* lp = a.parts_lse + r0 * a.pl_s0 + r1 * a.pl_s1 + r2 * a.pl_s2;
     const TP* op = (const TP*)a.parts_out + r0 * a.po_s0 + r1 * a.po_s1 + r2 * a.po_s2 + sub * VEC;
 
-    // 1. row max of the partial LSEs
-    float M = -INFINITY;
-    if (live)
-        for (int s = t; s < a.num_parts; s += T) M = fmaxf(M, lp[(int64_t)s * a.pl_part]);
-    const int wspan = T < 64 ? T : 64;
-    for (int off = wspan / 2; off > 0; off >>= 1) M = fmaxf(M, xor_shfl(M, off));
-    if (T > 64) {
-        if (lane == 0) wmax[tid >> 6] = M;
-        __syncthreads();
-        const int w0 = rib * (T / 64);  // the waves of this row
-        M = wmax[w0];
-        for (int w = 1; w < T / 64; ++w) M = fmaxf(M, wmax[w0 + w]);
-    }
-    const float Mu = M == -INFINITY ? 0.f : M;
-
-    // 2. weighted sum over this part-group's parts
+    // 1. online merge over this part-group's parts
+    float M = -INFINITY, W = 0.f;
     float acc[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) acc[j] = 0.f;
-    float W = 0.f;
     if (live) {
-        int s = pg;
-        for (; s + 3 * P < a.num_parts; s += 4 * P) {  // four parts in flight
+        const int S = a.num_parts;
+        for (int s = pg; s < S; s += 4 * P) {
             float x[4][VEC], l[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                l[u] = lp[(int64_t)(s + u * P) * a.pl_part];
-                PartLoad<TP>::load(op + (int64_t)(s + u * P) * a.po_part, x[u]);
+                const int sp = min(s + u * P, S - 1);   // past the end: a real part, weight 0
+                l[u] = lp[(int64_t)sp * a.pl_part];
+                PartLoad<TP>::load(op + (int64_t)sp * a.po_part, x[u]);
             }
+            float mg = -INFINITY;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const float w = fast_exp2(l[u] - Mu);
+                if (s + u * P >= S) l[u] = -INFINITY;
+                mg = fmaxf(mg, l[u]);
+            }
+            const float Mn = fmaxf(M, mg);
+            if (Mn == -INFINITY) continue;              // no part with a key so far
+            const float sc = fast_exp2(M - Mn);         // 0 while M is still -inf
+            W *= sc;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) acc[j] *= sc;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float w = fast_exp2(l[u] - Mn);   // -inf parts: 0
                 W += w;
 #pragma unroll
                 for (int j = 0; j < VEC; ++j) acc[j] += w * x[u][j];
             }
-        }
-        for (; s + P < a.num_parts; s += 2 * P) {
-            const float l0 = lp[(int64_t)s * a.pl_part], l1 = lp[(int64_t)(s + P) * a.pl_part];
-            float x0[VEC], x1[VEC];
-            PartLoad<TP>::load(op + (int64_t)s * a.po_part, x0);
-            PartLoad<TP>::load(op + (int64_t)(s + P) * a.po_part, x1);
-            const float w0 = fast_exp2(l0 - Mu), w1 = fast_exp2(l1 - Mu);
-            W += w0 + w1;
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) acc[j] += w0 * x0[j] + w1 * x1[j];
-        }
-        if (s < a.num_parts) {
-            const float l0 = lp[(int64_t)s * a.pl_part];
-            float x0[VEC];
-            PartLoad<TP>::load(op + (int64_t)s * a.po_part, x0);
-            const float w0 = fast_exp2(l0 - Mu);
-            W += w0;
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) acc[j] += w0 * x0[j];
+            M = Mn;
         }
     }
 
-    // 3. add the part-groups
+    // 2. combine the part-groups
     if (P > 1) {
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) red[tid * (VEC + 1) + j] = acc[j];
-        red[tid * (VEC + 1) + VEC] = W;
+        for (int j = 0; j < VEC; ++j) red[tid * RS + j] = acc[j];
+        red[tid * RS + VEC] = W;
+        red[tid * RS + VEC + 1] = M;
         __syncthreads();
         if (pg != 0) return;
-        for (int g = 1; g < P; ++g) {
-            const float* o = &red[(tid + g * LPR) * (VEC + 1)];
+        float Mt = M;
+        for (int g = 1; g < P; ++g) Mt = fmaxf(Mt, red[(tid + g * LPR) * RS + VEC + 1]);
+        if (Mt != -INFINITY) {
+            const float s0 = fast_exp2(M - Mt);
+            W *= s0;
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) acc[j] += o[j];
-            W += o[VEC];
+            for (int j = 0; j < VEC; ++j) acc[j] *= s0;
+            for (int g = 1; g < P; ++g) {
+                const float* o = &red[(tid + g * LPR) * RS];
+                const float sg = fast_exp2(o[VEC + 1] - Mt);
+                W += sg * o[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) acc[j] += sg * o[j];
+            }
         }
+        M = Mt;
     }
     if (!live) return;
     const float inv = W > 0.f ? 1.f / W : 0.f;

@@ -38,9 +38,21 @@ __global__ __launch_bounds__(256) void sage_quant_kernel(SageQuantArgs a) {
     const int H = is_q ? a.Hq : a.Hkv;
     const int S = is_q ? a.Sq : a.Sk;
     const int nblk = (S + 31) / 32;
-    const int blk = (int)(it % nblk);
-    const int64_t bh = it / nblk;     // b * H + h
-    const int b = (int)(bh / H), h = (int)(bh % H);
+    // item -> (b, h, block); 32-bit division whenever the item count allows it
+    int blk, b, h;
+    int64_t bh;                       // b * H + h
+    if (a.q_items + a.k_items <= 0xffffffffll) {
+        const uint32_t u = (uint32_t)it, q = u / (uint32_t)nblk;
+        blk = (int)(u - q * (uint32_t)nblk);
+        bh = q;
+        b = (int)(q / (uint32_t)H);
+        h = (int)(q - (uint32_t)b * (uint32_t)H);
+    } else {
+        blk = (int)(it % nblk);
+        bh = it / nblk;
+        b = (int)(bh / H);
+        h = (int)(bh % H);
+    }
     const int g = is_q ? h / (a.Hq / a.Hkv) : h;
     const uint16_t* src = (const uint16_t*)(is_q ? a.q : a.k) + (int64_t)b * a.x_batch[is_q ? 0 : 1] +
                           (int64_t)h * a.x_head[is_q ? 0 : 1];
