@@ -120,7 +120,7 @@ hipError_t launch_fmha(const FmhaArgs& a, int dtype, int D, bool causal, bool va
                        int grid_m, int grid_b, hipStream_t stream);
 hipError_t launch_kmean(const KmeanArgs& a, int dtype, int D, bool varlen, int grid_b,
                         hipStream_t stream);
-constexpr int kMaxDecodeSplits = 256;  // single-launch decode: its merge walks S / 8 round trips
+constexpr int kMaxDecodeSplits = 256;  // single-launch decode: its merge walks S / 16 round trips
 hipError_t launch_splitkv(const SplitArgs& a, int dtype, int D, bool fused, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int parts_dtype, int out_dtype, int D,
                         hipStream_t stream);
