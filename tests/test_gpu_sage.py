@@ -190,3 +190,20 @@ def test_sage_fwd_graph_replays(skv):
                                   causal=True, smooth_k=True)
         assert_lse_close(lse.cpu().numpy(), rl, f"lse, replay with seed {seed}")
         assert_out_close(out.float().cpu().numpy(), ro, f"out, replay with seed {seed}")
+
+
+def test_dense_d128_bench_shape_full_size(skv):
+    """B1 Hq32 Hkv8 S8192 D128 bf16, non-causal, smoothing on, K offset by +1 (the dense
+    problem bench.py times, with an offset so smoothing matters): sampled rows against
+    the oracle's INT8 path; every row finite."""
+    p = wl.attn_problem(1, 32, 8, 8192, 8192, 128, seed=7, k_offset=1.0)
+    o, l = _run(skv, p, False, True)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    g = np.random.default_rng(9)
+    rows = sorted({(0, int(g.integers(32)), int(g.integers(8192))) for _ in range(32)}
+                  | {(0, 0, 0), (0, 31, 8191)})
+    rows = np.array(rows, np.int64)
+    ro, rl = oracle.sage_attn(wl.bits(p.q), wl.bits(p.k), wl.bits(p.v), "bf16", scale=p.scale,
+                              smooth_k=True, rows=rows)
+    assert_lse_close(np.array([l[b, h, i] for b, h, i in rows]), rl)
+    assert_out_close(np.stack([o[b, h, i] for b, h, i in rows]), ro)
