@@ -64,12 +64,11 @@ __device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
 // has to pull in.  The merge keeps memory latency off serial chains: each thread
 // owns Q adjacent 4-column groups of one row and reads the partial LSEs and outputs
 // of GS chunks per round trip (4, 8 or 16: the smallest that covers the split
-// count, up to 16), all issued together.  Across groups of GS it keeps a running max
-// M of the chunk LSEs and rescales its sums by
-// 2^(M_old - M_new) when M grows; the result is the stable merge -- out =
-// sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), lse = M + log2 of that sum -- with
-// no exponent above 0.  Chunks with lse = -inf get weight 0; if every chunk is
-// -inf the row gets (0, -inf).
+// count, up to 16), all issued together.  Across groups of GS it keeps a running
+// max M of the chunk LSEs and rescales its sums by 2^(M_old - M_new) when M grows;
+// the result is the stable merge -- out = sum_s 2^(lse_s - M) o_s / sum_s
+// 2^(lse_s - M), lse = M + log2 of that sum -- with no exponent above 0.  Chunks
+// with lse = -inf get weight 0; if every chunk is -inf the row gets (0, -inf).
 template <typename T, int D, int GS>
 __device__ __forceinline__ void merge_rows(const SplitArgs& a, int b, int hk, int R, int G);
 
