@@ -441,10 +441,16 @@ KERNEL_SOURCES = [os.path.join(ROOT, "split_kv_merge_amd", "csrc", f)
 
 
 def kernel_source_sha():
+    """SHA-256 of the decode kernel's sources with comments and whitespace removed,
+    so that the counter record goes stale when the code changes, not its comments."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
