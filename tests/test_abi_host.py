@@ -206,3 +206,66 @@ def test_splitkv_decode_rejects(lib):
     rows = 8 * 2 * 32
     # 16-bit chunk outputs, float32 chunk LSEs, one int32 ticket per (batch, kv head)
     assert need == ((rows * 128 * 2 + 255) // 256 + (rows * 4 + 255) // 256 + 1) * 256
+
+
+def _sage_fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=128,
+             dtype=0, layout=0, scale=0.1, causal=0, smooth=1, ws=ctypes.c_void_p(0x20000),
+             wsb=1 << 30)
+    a.update(kw)
+    return lib.skv_sage_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                            a["Sq"], a["Sk"], a["D"], a["dtype"], a["layout"], a["scale"],
+                            a["causal"], a["smooth"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=256), 2),                 # the INT8 path is built for D 64 and 128
+    (dict(D=96), 2),
+    (dict(dtype=2), 2),
+    (dict(Hq=5), 1),
+    (dict(q=None), 1),
+    (dict(out=None), 1),
+    (dict(ws=None), 1),
+    (dict(ws=ctypes.c_void_p(0x20010)), 1),   # not 256-byte aligned
+    (dict(wsb=16), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(layout=3), 1),
+    (dict(Sq=65536 * 256), 2),        # more row tiles than the grid allows
+])
+def test_sage_fwd_rejects(lib, kw, status):
+    assert _sage_fwd(lib, **kw) == status
+    assert lib.skv_last_error() != b""
+
+
+def test_sage_zero_sized_and_workspace(lib):
+    assert _sage_fwd(lib, B=0) == 0
+    assert _sage_fwd(lib, Sq=0) == 0
+    # sections, each padded to 256 bytes: mean(k) fp32 [B,Hkv,D]; its fp64 split sums
+    # (32 splits for 2 kv heads); q codes int8; q scales fp32 [B,Hq,Sq/32]; add-back fp32
+    # [B,Hq,Sq]; k codes int8; k scales fp32; V in fp16 (bf16 input)
+    r = lambda x: (x + 255) // 256 * 256
+    B, Hq, Hkv, Sq, Sk, D = 1, 4, 2, 64, 64, 128
+    want = (r(B * Hkv * D * 4) + r(B * Hkv * 32 * D * 8) + r(B * Hq * Sq * D) + r(B * Hq * 2 * 4)
+            + r(B * Hq * Sq * 4) + r(B * Hkv * Sk * D) + r(B * Hkv * 2 * 4) + r(B * Hkv * Sk * D * 2))
+    assert lib.skv_sage_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, 0, 1) == want
+    # fp16 input: no V copy; no smoothing: no mean(k) and no add-back
+    assert lib.skv_sage_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, 1, 0) == (
+        r(B * Hq * Sq * D) + r(B * Hq * 2 * 4) + r(B * Hkv * Sk * D) + r(B * Hkv * 2 * 4))
+
+
+def test_sage_quant_rejects(lib):
+    P = FAKE
+
+    def call(**kw):
+        a = dict(q=P, k=P, B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=128, smooth=1, qc=P, qs=P, kc=P,
+                 ks=P, kb=P)
+        a.update(kw)
+        return lib.skv_sage_quant(a["q"], a["k"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"],
+                                  a["D"], 0, 0, a["smooth"], a["qc"], a["qs"], a["kc"], a["ks"],
+                                  a["kb"], None)
+    assert call(kb=None) == 1         # smoothing needs the mean(k) output
+    assert call(qc=None) == 1
+    assert call(qc=ctypes.c_void_p(0x10008)) == 1   # codes need 16-byte alignment
+    assert call(D=256) == 2
+    assert call(Hkv=3) == 1
+    assert call(B=0) == 0
