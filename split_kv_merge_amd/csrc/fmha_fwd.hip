@@ -52,6 +52,9 @@ template <int D> struct FmhaTile {
     // dwords) touches all 64 banks once.
     static constexpr int VLD = D + 32;
     static constexpr int NCH = BN * D / 8 / NT;    // 16-byte chunks per thread per tile
+    // Row pitch (elements) of each wave's Q / O staging slice: the operand reads of
+    // Q use the conflict-free pattern of the K reads.
+    static constexpr int QLD = D + 8;
 };
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
@@ -64,6 +67,7 @@ void fmha_fwd_kernel(FmhaArgs a) {
     typedef typename E::vec8 V8;
     typedef FmhaTile<D> Tl;
     constexpr int BM = Tl::BM, BN = Tl::BN, KLD = Tl::KLD, VLD = Tl::VLD, NCH = Tl::NCH;
+    constexpr int QLD = Tl::QLD;
     constexpr int NKK = D / 16;   // MFMA k-steps over the head dimension
     constexpr int NJB = BN / 32;  // 32-key blocks per tile
     constexpr int NDB = D / 32;   // 32-wide blocks of the output head dimension
@@ -71,8 +75,11 @@ void fmha_fwd_kernel(FmhaArgs a) {
 
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KLD];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN * VLD];
+    // One slice per wave: its 32 rows of Q on the way in, of O on the way out.
+    __shared__ __attribute__((aligned(16))) uint16_t qo_lds[Tl::NW][32 * QLD];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int n = lane & 31, hg = lane >> 5;
     // Grid (head, batch | sequence, row tile), dispatched head-fastest: with causal
     // masking the row tiles run last-first, so the work groups go out in order of
@@ -112,38 +119,24 @@ void fmha_fwd_kernel(FmhaArgs a) {
     // mirrored blocks (w and 7 - w), so in the causal diagonal band, where later
     // blocks see more keys, every SIMD carries about the same work.
     const int rblk = (Tl::NW == 8 && wave >= 4) ? 11 - wave : wave;
-    const int row = m0 + rblk * 32 + n;
+    const int wrow0 = m0 + rblk * 32;
+    const int row = wrow0 + n;
     const bool row_ok = row < Lq;
 
-    // Q as the B operand: this lane holds q[row][hg*D/2 + 8kk .. +8) for each k-step.
-    V8 qf[NKK];
-    {
-        const uint16_t* qr = qp + (int64_t)row * a.q_row + hg * (D / 2);
+    // The wave's 32 rows of Q and O move between global memory and its LDS slice
+    // in whole rows: chunk c of a lane is the 16-byte chunk c * 64 + lane of the
+    // slice, so consecutive lanes cover consecutive bytes of a row (one load or store
+    // instruction spans 1 KB of rows instead of 64 scattered pieces).
+    constexpr int QCH = 32 * CPR / 64;  // 16-byte chunks per lane
+    constexpr int RPC = 64 / CPR;       // rows per chunk step
+    const int lrow = lane / CPR, lcol = (lane % CPR) * 8;
+    uint16_t* qs = qo_lds[wave];
+    uint16_t* const qsl = qs + lrow * QLD + lcol;  // chunk c of this lane: qsl + c * RPC * QLD
+    // Q rows past the end read the last row: finite data whose results are never stored.
+    u32x4 qraw[QCH];
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (row_ok) raw = load16(qr + kk * 8);
-            qf[kk] = as_vec8<T>(raw);
-        }
-    }
-
-    // Smoothing bias in log2 units: scale*log2(e) * (q_row . mean(k)).
-    float bias = 0.f;
-    if (a.kbar) {
-        const float* kb = a.kbar + ((int64_t)b * a.Hkv + g) * D + hg * (D / 2);
-        float acc = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            u32x4 raw = __builtin_bit_cast(u32x4, qf[kk]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc += E::to_float((uint16_t)(raw[j] & 0xffff)) * kb[kk * 8 + 2 * j];
-                acc += E::to_float((uint16_t)(raw[j] >> 16)) * kb[kk * 8 + 2 * j + 1];
-            }
-        }
-        acc += xor_shfl(acc, 32);
-        bias = acc * a.scale_log2;
-    }
+    for (int c = 0; c < QCH; ++c)
+        qraw[c] = load16(qp + (int64_t)min(wrow0 + c * RPC + lrow, Lq - 1) * a.q_row + lcol);
 
     // Keys this tile of rows can see.
     int kv_end = Lk;
@@ -158,22 +151,11 @@ void fmha_fwd_kernel(FmhaArgs a) {
     // the wave's last row, or any tile of a wave whose rows all lie past Lq, would
     // only add masked (-inf) logits -- exactly nothing -- so the wave skips its math
     // there (it still stages tiles and joins every barrier).
-    const int wrow0 = m0 + rblk * 32;
     int wave_tiles = ntiles;
     if (wrow0 >= Lq)
         wave_tiles = 0;
     else if (CAUSAL)
         wave_tiles = min(ntiles, max(0, (min(wrow0 + 31, Lq - 1) + diag + BN) / BN));
-
-    f32x16 o[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-    // Online softmax with a lazily moved reference max m_ref (log2 units, smoothed
-    // logits): it only moves when a tile's max exceeds it by more than kTau, so most
-    // tiles skip rescaling O and l.  Every p = 2^(s - m_ref) stays <= 2^kTau.
-    constexpr float kTau = 8.f;
-    float m_ref = -INFINITY, l_run = 0.f;
-    const float c = a.scale_log2;
 
     // K/V tile loads: chunk ci of this thread is key ch / CPR, column (ch % CPR) * 8,
     // ch = tid + NT ci; its offset inside a tile is a 32-bit constant and the tile
@@ -213,6 +195,45 @@ void fmha_fwd_kernel(FmhaArgs a) {
         }
     };
     const int full_tiles = Lk / BN;  // tiles with no key past the end
+
+    // The first tile's loads go out while Q is still in flight.
+    if (ntiles > 0) load_tile(0, 0 >= full_tiles);
+
+    // Q as the B operand: this lane holds q[row][hg*D/2 + 8kk .. +8) for each k-step,
+    // read back from the slice (a wave's LDS accesses complete in order).
+#pragma unroll
+    for (int c = 0; c < QCH; ++c) store16(qsl + c * RPC * QLD, qraw[c]);
+    V8 qf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_vec8<T>(load16(&qs[n * QLD + hg * (D / 2) + kk * 8]));
+
+    // Smoothing bias in log2 units: scale*log2(e) * (q_row . mean(k)).
+    float bias = 0.f;
+    if (a.kbar) {
+        const float* kb = a.kbar + ((int64_t)b * a.Hkv + g) * D + hg * (D / 2);
+        float acc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            u32x4 raw = __builtin_bit_cast(u32x4, qf[kk]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc += E::to_float((uint16_t)(raw[j] & 0xffff)) * kb[kk * 8 + 2 * j];
+                acc += E::to_float((uint16_t)(raw[j] >> 16)) * kb[kk * 8 + 2 * j + 1];
+            }
+        }
+        acc += xor_shfl(acc, 32);
+        bias = acc * a.scale_log2;
+    }
+
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+    // Online softmax with a lazily moved reference max m_ref (log2 units, smoothed
+    // logits): it only moves when a tile's max exceeds it by more than kTau, so most
+    // tiles skip rescaling O and l.  Every p = 2^(s - m_ref) stays <= 2^kTau.
+    constexpr float kTau = 8.f;
+    float m_ref = -INFINITY, l_run = 0.f;
+    const float c = a.scale_log2;
 
     // Lane roles for the transpose read of V^T operands.
     const int g16 = lane >> 4, e4 = (lane & 15) >> 2, q4 = lane & 3;
@@ -334,11 +355,11 @@ void fmha_fwd_kernel(FmhaArgs a) {
 
     // Two LDS buffers: tile t is computed from buffer t&1 while tile t+1 is stored
     // into the other one and tile t+2 is being loaded; one barrier per tile.
-    if (ntiles > 0) {
-        load_tile(0, 0 >= full_tiles);
-        store_tile(0);
-        if (ntiles > 1) load_tile(1, 1 >= full_tiles);
-    }
+    if (ntiles > 0) store_tile(0);
+    // Every load so far (Q, tile 0) has landed on every path into the loop, so the
+    // compiler's wait counts inside it cover only the tile loads in flight.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    if (ntiles > 1) load_tile(1, 1 >= full_tiles);
     __syncthreads();
     const int nfree = min(first_masked, ntiles);
     int t = 0;
@@ -348,22 +369,28 @@ void fmha_fwd_kernel(FmhaArgs a) {
     // Epilogue: out = O / l; LSE = m_ref + log2(l) (+ smoothing bias), one store per row.
     const float l_tot = l_run + xor_shfl(l_run, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (row_ok) {
-        uint16_t* op = (uint16_t*)a.out + q_off + (int64_t)h * a.q_head + (int64_t)row * a.q_row;
+    // O^T columns into the slice as rows, then out in whole rows.
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int d = db * 32 + 8 * a4 + hg * 4;
-                u32x2 w;
-                w.x = E::pack2(o[db][4 * a4 + 0] * inv, o[db][4 * a4 + 1] * inv);
-                w.y = E::pack2(o[db][4 * a4 + 2] * inv, o[db][4 * a4 + 3] * inv);
-                *reinterpret_cast<u32x2*>(op + d) = w;
-            }
-        if (hg == 0 && a.lse)
-            a.lse[lse_off + (int64_t)h * a.lse_head + row] =
-                l_tot > 0.f ? m_ref + fast_log2(l_tot) + bias : -INFINITY;
+        for (int a4 = 0; a4 < 4; ++a4) {
+            const int d = db * 32 + 8 * a4 + hg * 4;
+            u32x2 w;
+            w.x = E::pack2(o[db][4 * a4 + 0] * inv, o[db][4 * a4 + 1] * inv);
+            w.y = E::pack2(o[db][4 * a4 + 2] * inv, o[db][4 * a4 + 3] * inv);
+            *reinterpret_cast<u32x2*>(&qs[n * QLD + d]) = w;
+        }
+    uint16_t* const op = (uint16_t*)a.out + q_off + (int64_t)h * a.q_head +
+                         (int64_t)(wrow0 + lrow) * a.q_row + lcol;
+    const int rows_left = Lq - wrow0 - lrow;  // this lane's rows c * RPC below it exist
+#pragma unroll
+    for (int c = 0; c < QCH; ++c) {
+        const u32x4 w = load16(qsl + c * RPC * QLD);
+        if (c * RPC < rows_left) store16(op + (int64_t)c * RPC * a.q_row, w);
     }
+    if (row_ok && hg == 0 && a.lse)
+        a.lse[lse_off + (int64_t)h * a.lse_head + row] =
+            l_tot > 0.f ? m_ref + fast_log2(l_tot) + bias : -INFINITY;
 }
 
 template <typename T, int D>
