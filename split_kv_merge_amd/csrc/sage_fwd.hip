@@ -48,6 +48,7 @@ template <int D> struct SageTile {
     static constexpr int VLD = D + 32;             // V row pitch in LDS (fp16 elements)
     static constexpr int KCH = BN * D / 16 / NT;   // 16-byte K chunks per thread per tile
     static constexpr int VCH = BN * D / 8 / NT;    // 16-byte V chunks per thread per tile
+    static constexpr int OLD = D + 8;              // O row pitch in a wave's slice (elements)
 };
 
 constexpr int kMagic = 0x4B400000;                 // bit pattern of 1.5 * 2^23
@@ -68,8 +69,12 @@ void sage_fwd_kernel(SageFwdArgs a) {
 
     __shared__ __attribute__((aligned(16))) int8_t k_lds[2][BN * KLD];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN * VLD];
+    // One slice per wave: its 32 rows of Q codes on the way in (pitch KLD bytes, the
+    // conflict-free pattern of the K reads), of O on the way out (pitch OLD).
+    __shared__ __attribute__((aligned(16))) uint16_t qo_lds[Tl::NW][32 * Tl::OLD];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int n = lane & 31, hg = lane >> 5;
     // grid (head, batch, row tile), head-fastest, causal row tiles last-first
     const int h = blockIdx.x, b = blockIdx.y;
@@ -90,17 +95,29 @@ void sage_fwd_kernel(SageFwdArgs a) {
     const int row = wrow0 + n;
     const bool row_ok = row < Lq;
 
-    // Q codes as the B operand: lane holds q^[row][hg*D/2 + 16kk .. +16) per k-step.
-    i32x4 qf[NKK];
+    // The wave's 32 rows of Q codes come in, and its 32 rows of O go out, in whole
+    // rows through its LDS slice: consecutive lanes take consecutive 16-byte chunks
+    // of a row, so each instruction covers 1 KB of rows.  Rows past the end read the
+    // last row (finite codes whose results are never stored).
+    uint16_t* qs = qo_lds[wave];
+    int8_t* qsb = reinterpret_cast<int8_t*>(qs);
+    constexpr int QCPR = D / 16, QRPC = 64 / QCPR, QCH = 32 / QRPC;  // Q code chunks
     {
-        const int8_t* qr = a.q_codes + (bh * Lq + row) * D + hg * (D / 2);
+        const int lr = lane / QCPR, lc = (lane % QCPR) * 16;
+        const int8_t* qb = a.q_codes + bh * Lq * D + lc;
+        u32x4 qraw[QCH];
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (row_ok) raw = load16(qr + kk * 16);
-            qf[kk] = __builtin_bit_cast(i32x4, raw);
-        }
+        for (int c = 0; c < QCH; ++c)
+            qraw[c] = load16(qb + (int64_t)min(wrow0 + c * QRPC + lr, Lq - 1) * D);
+#pragma unroll
+        for (int c = 0; c < QCH; ++c) store16(qsb + (c * QRPC + lr) * KLD + lc, qraw[c]);
     }
+    // Q codes as the B operand: lane holds q^[row][hg*D/2 + 16kk .. +16) per k-step
+    // (a wave's LDS accesses complete in order).
+    i32x4 qf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+        qf[kk] = __builtin_bit_cast(i32x4, load16(qsb + n * KLD + hg * (D / 2) + kk * 16));
     const float cq = wrow0 < Lq ? a.scale_log2 * a.q_scale[bh * nq + wrow0 / 32] : 0.f;
     const float bias = (a.q_bias && row_ok) ? a.q_bias[bh * Lq + row] : 0.f;
 
@@ -281,8 +298,11 @@ void sage_fwd_kernel(SageFwdArgs a) {
     if (ntiles > 0) {
         load_tile(0, 0 >= full_tiles);
         store_tile(0);
-        if (ntiles > 1) load_tile(1, 1 >= full_tiles);
     }
+    // Every load so far has landed on every path into the loop, so the compiler's
+    // wait counts inside it cover only the tile loads in flight.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    if (ntiles > 1) load_tile(1, 1 >= full_tiles);
     __syncthreads();
     const int nfree = min(first_masked, ntiles);
     int t = 0;
@@ -291,22 +311,29 @@ void sage_fwd_kernel(SageFwdArgs a) {
 
     const float l_tot = l_run + xor_shfl(l_run, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (row_ok) {
-        uint16_t* op = (uint16_t*)a.out + (int64_t)b * a.o_batch + (int64_t)h * a.o_head +
-                       (int64_t)row * a.o_row;
+    // O^T columns into the slice as rows, then out in whole rows.
+    constexpr int OLD = Tl::OLD, OCPR = D / 8, ORPC = 64 / OCPR, OCH = 32 / ORPC;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int d = db * 32 + 8 * a4 + hg * 4;
-                u32x2 w;
-                w.x = EO::pack2(o[db][4 * a4 + 0] * inv, o[db][4 * a4 + 1] * inv);
-                w.y = EO::pack2(o[db][4 * a4 + 2] * inv, o[db][4 * a4 + 3] * inv);
-                *reinterpret_cast<u32x2*>(op + d) = w;
-            }
-        if (hg == 0 && a.lse)
-            a.lse[bh * Lq + row] = l_tot > 0.f ? m_ref + fast_log2(l_tot) + bias : -INFINITY;
+        for (int a4 = 0; a4 < 4; ++a4) {
+            const int d = db * 32 + 8 * a4 + hg * 4;
+            u32x2 w;
+            w.x = EO::pack2(o[db][4 * a4 + 0] * inv, o[db][4 * a4 + 1] * inv);
+            w.y = EO::pack2(o[db][4 * a4 + 2] * inv, o[db][4 * a4 + 3] * inv);
+            *reinterpret_cast<u32x2*>(&qs[n * OLD + d]) = w;
+        }
+    const int lr = lane / OCPR, lc = (lane % OCPR) * 8;
+    uint16_t* const op = (uint16_t*)a.out + (int64_t)b * a.o_batch + (int64_t)h * a.o_head +
+                         (int64_t)(wrow0 + lr) * a.o_row + lc;
+    const int rows_left = Lq - wrow0 - lr;  // this lane's rows c * ORPC below it exist
+#pragma unroll
+    for (int c = 0; c < OCH; ++c) {
+        const u32x4 w = load16(qs + (c * ORPC + lr) * OLD + lc);
+        if (c * ORPC < rows_left) store16(op + (int64_t)c * ORPC * a.o_row, w);
     }
+    if (row_ok && hg == 0 && a.lse)
+        a.lse[bh * Lq + row] = l_tot > 0.f ? m_ref + fast_log2(l_tot) + bias : -INFINITY;
 }
 
 template <typename T, int D>
