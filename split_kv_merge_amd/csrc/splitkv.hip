@@ -222,9 +222,10 @@ void splitkv_kernel(SplitArgs a) {
     const uint16_t* kp = (const uint16_t*)a.k + (int64_t)b * a.kv_batch + (int64_t)hk * a.kv_head;
     const uint16_t* vp = (const uint16_t*)a.v + (int64_t)b * a.kv_batch + (int64_t)hk * a.kv_head;
 
-    // Loads of one block into a register buffer.  Rows past the chunk end are
-    // clamped to its last key (real, finite data; the chunk is non-empty whenever a
-    // block exists) and masked out of the softmax, so no load needs a branch.
+    // Loads of one block into a register buffer, as streaming (nontemporal) loads:
+    // every K/V byte is read once.  Rows past the chunk end are clamped to its last
+    // key (real, finite data; the chunk is non-empty whenever a block exists) and
+    // masked out of the softmax, so no load needs a branch.
     typedef u32x4 KBuf[NHF][NKK];
     typedef u32x4 VBuf[VCH];
     auto load_block = [&](KBuf& kb_, VBuf& vb_, int blk) {
@@ -234,13 +235,13 @@ void splitkv_kernel(SplitArgs a) {
             const int j = min(kb + hf * 16 + n, j1 - 1);
             const uint16_t* kr = kp + (int64_t)j * a.kv_row + g4 * 8;
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) kb_[hf][kk] = load16(kr + kk * 32);
+            for (int kk = 0; kk < NKK; ++kk) kb_[hf][kk] = load16_stream(kr + kk * 32);
         }
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = lane + 64 * u;
             const int j = min(kb + c / CPR, j1 - 1);
-            vb_[u] = load16(vp + (int64_t)j * a.kv_row + (c % CPR) * 8);
+            vb_[u] = load16_stream(vp + (int64_t)j * a.kv_row + (c % CPR) * 8);
         }
     };
 
