@@ -225,14 +225,16 @@ void splitkv_kernel(SplitArgs a) {
     // Loads of one block into a register buffer, as streaming (nontemporal) loads:
     // every K/V byte is read once.  Rows past the chunk end are clamped to its last
     // key (real, finite data; the chunk is non-empty whenever a block exists) and
-    // masked out of the softmax, so no load needs a branch.
+    // masked out of the softmax, so no load needs a branch.  A prefetch past the
+    // wave's last block (`idle`) reads only the chunk's first key row: the same
+    // instructions, so the wait counts stay the same, but no second pass over a block.
     typedef u32x4 KBuf[NHF][NKK];
     typedef u32x4 VBuf[VCH];
-    auto load_block = [&](KBuf& kb_, VBuf& vb_, int blk) {
+    auto load_block = [&](KBuf& kb_, VBuf& vb_, int blk, bool idle) {
         const int kb = j0 + blk * KPB;
 #pragma unroll
         for (int hf = 0; hf < NHF; ++hf) {
-            const int j = min(kb + hf * 16 + n, j1 - 1);
+            const int j = idle ? j0 : min(kb + hf * 16 + n, j1 - 1);
             const uint16_t* kr = kp + (int64_t)j * a.kv_row + g4 * 8;
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) kb_[hf][kk] = load16_stream(kr + kk * 32);
@@ -240,7 +242,7 @@ void splitkv_kernel(SplitArgs a) {
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = lane + 64 * u;
-            const int j = min(kb + c / CPR, j1 - 1);
+            const int j = idle ? j0 : min(kb + c / CPR, j1 - 1);
             vb_[u] = load16_stream(vp + (int64_t)j * a.kv_row + (c % CPR) * 8);
         }
     };
@@ -320,18 +322,18 @@ void splitkv_kernel(SplitArgs a) {
 
     // Ping-pong between two register buffers: the loads of the wave's next block
     // are in flight while the current one is computed.  The prefetch is issued
-    // unconditionally (past the wave's last block it re-reads the current block,
-    // an L2 hit) and never copied between registers, so the compiler's wait counts
-    // only cover the older group of loads.
+    // unconditionally (past the wave's last block it reads one key row) and never
+    // copied between registers, so the compiler's wait counts only cover the older
+    // group of loads.
     KBuf ka, kb2;
     VBuf va, vb2;
-    if (wave < nblk) load_block(ka, va, wave);
+    if (wave < nblk) load_block(ka, va, wave, false);
     for (int blk = wave; blk < nblk; blk += 2 * kWaves) {
         const int nxt = blk + kWaves;
-        load_block(kb2, vb2, nxt < nblk ? nxt : blk);
+        load_block(kb2, vb2, nxt, nxt >= nblk);
         compute_block(ka, va, blk);
         if (nxt >= nblk) break;
-        load_block(ka, va, nxt + kWaves < nblk ? nxt + kWaves : nxt);
+        load_block(ka, va, nxt + kWaves, nxt + kWaves >= nblk);
         compute_block(kb2, vb2, nxt);
     }
 
