@@ -1,7 +1,7 @@
 // ceilings.hip -- micro-benchmarks for the practical ceilings the attention kernels
 // are measured against on MI355X (gfx950): LDS read bandwidth (16-byte reads and
 // the 64-bit transpose read), bf16 MFMA throughput, v_exp_f32 and v_fma_f32 issue
-// rates, and a plain HBM read stream.  Measurement infrastructure only; nothing
+// rates, and an HBM read stream (plain and nontemporal loads).  Measurement infrastructure only; nothing
 // in the attention library uses it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -83,17 +83,22 @@ __global__ __launch_bounds__(256) void fma_f32(float* out, int iters) {
   float r = x0 + x1 + x2 + x3 + x4 + x5 + x6 + x7;
   if (r == 1234.5f) out[blockIdx.x] = r;
 }
-// HBM read stream: 16 B loads, grid-stride
+// HBM read stream: each work group streams its own contiguous range with eight
+// 16-byte loads in flight per thread, as plain loads or with the nontemporal hint.
+template <bool NT>
 __global__ __launch_bounds__(256) void hbm_read(const u32x4* in, int64_t n, uint32_t* out) {
   u32x4 acc = {0,0,0,0};
-  int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    u32x4 a = __builtin_nontemporal_load(in + i), b = __builtin_nontemporal_load(in + i + stride);
-    u32x4 c = __builtin_nontemporal_load(in + i + 2*stride), d = __builtin_nontemporal_load(in + i + 3*stride);
-    acc ^= a ^ b ^ c ^ d;
+  const int64_t C = n / gridDim.x;
+  const u32x4* p = in + (int64_t)blockIdx.x * C;
+  int64_t i = threadIdx.x;
+  for (; i + 7 * 256 < C; i += 8 * 256) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = NT ? __builtin_nontemporal_load(p + i + u * 256) : p[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
   }
-  for (; i < n; i += stride) acc ^= in[i];
+  for (; i < C; i += 256) acc ^= p[i];
   if (acc.x == 0x12345678) out[blockIdx.x] = acc.y;
 }
 extern "C" int run(int which, void* p, int64_t n, void* out, int grid, int iters, void* stream) {
@@ -104,7 +109,8 @@ extern "C" int run(int which, void* p, int64_t n, void* out, int grid, int iters
     case 2: hipLaunchKernelGGL(mfma_bf16, dim3(grid), dim3(256), 0, s, (float*)out, iters); break;
     case 3: hipLaunchKernelGGL(exp_f32, dim3(grid), dim3(256), 0, s, (float*)out, iters); break;
     case 4: hipLaunchKernelGGL(fma_f32, dim3(grid), dim3(256), 0, s, (float*)out, iters); break;
-    case 5: hipLaunchKernelGGL(hbm_read, dim3(grid), dim3(256), 0, s, (const u32x4*)p, n, (uint32_t*)out); break;
+    case 5: hipLaunchKernelGGL(hbm_read<false>, dim3(grid), dim3(256), 0, s, (const u32x4*)p, n, (uint32_t*)out); break;
+    case 6: hipLaunchKernelGGL(hbm_read<true>, dim3(grid), dim3(256), 0, s, (const u32x4*)p, n, (uint32_t*)out); break;
   }
   return (int)hipGetLastError();
 }

@@ -58,11 +58,12 @@ def measure():
     sec = t(4, g2, 2000)
     res["fma_f32_lanes_per_clk_per_cu"] = g2 * 256 * 8 * 2000 / sec / CU / CLK
     buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
-    best = 0.0
-    for grid in (2048, 4096, 8192):
-        sec = t(5, grid, 0, ctypes.c_void_p(buf.data_ptr()), buf.numel() // 16)
-        best = max(best, buf.numel() / sec / 1e9)
-    res["hbm_read_stream_GBs"] = best
+    for which, key in ((5, "hbm_read_stream_GBs"), (6, "hbm_read_stream_nontemporal_GBs")):
+        best = 0.0
+        for grid in (512, 1024, 2048, 4096, 8192):   # each divides the element count
+            sec = t(which, grid, 0, ctypes.c_void_p(buf.data_ptr()), buf.numel() // 16)
+            best = max(best, buf.numel() / sec / 1e9)
+        res[key] = best
     return res
 
 
