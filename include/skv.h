@@ -214,8 +214,8 @@ skv_status_t skv_merge_state(int num_parts, int R0, int R1, int R2, int D,
 size_t skv_workspace_bytes(int B_or_nseq, int Hkv, int D, int smooth_k);
 
 /* A split count for the split-KV calls: about one (batch, kv head, chunk) work
- * group per compute unit (256 CUs), two when chunks would exceed 4096 keys at
- * D <= 128, with chunks of at least 256 keys.  Pure host arithmetic; returns >= 1. */
+ * group per compute unit (256 CUs), with chunks of at least 256 keys (D and
+ * rows_per_kv_head do not change it at present).  Pure host arithmetic; returns >= 1. */
 int skv_pick_num_splits(int B, int Hkv, int rows_per_kv_head, int Lkv, int D);
 
 /*

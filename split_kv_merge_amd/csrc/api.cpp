@@ -116,17 +116,16 @@ size_t skv_workspace_bytes(int B_or_nseq, int Hkv, int D, int smooth_k) {
 
 int skv_pick_num_splits(int B, int Hkv, int rows_per_kv_head, int Lkv, int D) {
     (void)rows_per_kv_head;
+    (void)D;
     if (B <= 0 || Hkv <= 0 || Lkv <= 0) return 1;
     // One work group per compute unit (256 CUs) streams best: a launch then needs a
     // single round of work groups (every round pays the latency chain of loading
     // Q, the first blocks, the combine and the partial-state publish), and each wave
-    // keeps several blocks in flight.  Chunks longer than 4096 keys (D <= 128) are
-    // split once more, up to two work groups per CU.  Every chunk keeps at least 256
-    // keys (two 32-key blocks per wave).
+    // keeps several blocks in flight; with streaming loads one wave per SIMD keeps
+    // HBM busy even for long chunks.  Every chunk keeps at least 256 keys (two
+    // 32-key blocks per wave).
     const int64_t units = (int64_t)B * Hkv;
     int64_t s = (256 + units - 1) / units;
-    if (D <= 128)
-        while (2 * s * units <= 512 && (Lkv + s - 1) / s > 4096) s *= 2;
     int64_t smax = Lkv / 256;
     if (smax < 1) smax = 1;
     if (s > smax) s = smax;
