@@ -170,9 +170,10 @@ __device__ __forceinline__ void merge_rows(const SplitArgs& a, int b, int hk, in
 }
 
 template <typename T, int D, bool FUSED>
-// Two waves per SIMD (two work groups per compute unit) at D <= 128: the second wave
-// hides the first one's load and LDS latencies; without the hint the compiler spends
-// registers down to one wave per SIMD.  D = 256 needs the whole register file.
+// Up to two waves per SIMD (two work groups per compute unit) at D <= 128, so that
+// launches with more work groups than compute units still fill the chip; the usual
+// split count (skv_pick_num_splits) gives one work group per CU.  D = 256 needs the
+// whole register file.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 void splitkv_kernel(SplitArgs a) {
     using E = Elem<T>;
