@@ -26,7 +26,8 @@ namespace {
 
 constexpr int kWaves = 4;
 // Keys per block: 32, or 16 at D = 256, where two 32-key blocks in flight per wave
-// (K and V, 128 registers each) would not leave room for a second wave per SIMD.
+// (K and V, 128 registers each) would not fit in the register file beside the rest
+// of the wave's state (the D = 256 kernel already runs one wave per SIMD).
 template <int D> constexpr int keys_per_block() { return D == 256 ? 16 : 32; }
 
 template <int D> struct SplitLds {
