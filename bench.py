@@ -16,15 +16,22 @@ the per-chunk partial states and the last work group of each (batch, kv head)
 merges them.  `roofline` covers that kernel: its algorithmic bytes per launch over
 its average launch duration, timed with HIP events on the launch stream in a
 separate pass in which the launches are queued behind a spin kernel (so host
-overhead does not open gaps).  The two-kernel form (partials, then merge_state)
-is timed as well and reported per problem.
+overhead does not open gaps); per problem it reports the mean (`us`, the figure the
+roofline uses) and the 10th / 50th / 90th percentiles over the repetitions, and
+`step_us` gives the same spread for the captured step.  The two-kernel form
+(partials, then merge_state) is timed as well and reported per problem.
 `cpu_baseline` times the fp64 oracle (oracle/, C + OpenMP) on a bounded sample of
 the same workload.  `secondary` reports the other shapes of the same path
 (the decode on a partly filled KV cache bounded by a device kv_len, wide-head
 decode, varlen causal prefill, ring-style chunked prefill, a dense D128 prefill,
 the tiny LSE case) in us, GB/s or TFLOP/s and as a fraction of the roofline, plus
 the INT8 QK^T path (skv_sage_fwd, smoothing on) on the ring and dense problems, its
-fraction taken against the combined int8 + fp16 MFMA peak.
+fraction taken against the combined int8 + fp16 MFMA peak.  Secondary figures are
+the median (`us`) of 50 graph replays, each timed with its own HIP events, with
+p10 / p90 and the mean beside it.  `practical_ceilings` are the micro-benchmarks of
+microbench/ceilings.hip run in the same process (HBM read stream with plain and with
+nontemporal loads, bf16 MFMA, ...); every decode and prefill figure is also given
+as a fraction of them (`frac_practical`, `frac_mfma_practical`).
 """
 from __future__ import annotations
 
@@ -130,18 +137,42 @@ def capture(fn):
     return g
 
 
+def _pct(xs, q):
+    """q-th percentile (0..100) of a list, linear interpolation."""
+    ys = sorted(xs)
+    if not ys:
+        return float("nan")
+    pos = (len(ys) - 1) * q / 100.0
+    lo = int(pos)
+    hi = min(lo + 1, len(ys) - 1)
+    return ys[lo] + (ys[hi] - ys[lo]) * (pos - lo)
+
+
+def stats(xs):
+    """Mean, median and the 10th / 90th percentiles of per-replay times (us)."""
+    return dict(mean=sum(xs) / len(xs), p10=_pct(xs, 10), p50=_pct(xs, 50), p90=_pct(xs, 90))
+
+
 def time_graph(g, reps, warm=3):
-    """Mean GPU time (us) of one replay, from HIP events around `reps` replays."""
+    """Per-replay GPU times (us) of a captured graph: HIP events around each of `reps`
+    replays, all queued behind a spin kernel that outlasts the host's enqueue time, so
+    host overhead opens no gaps.  Returns stats(): mean, p10, p50, p90."""
     for _ in range(warm):
         g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
+    t0 = time.perf_counter()
+    g.replay()                      # host enqueue cost of one replay
+    host_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda._sleep(int(_spin_cycles_per_ms() * (3.0 * (host_ms + 0.05) * reps + 5.0)))
+    for a, b in evs:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return stats([a.elapsed_time(b) * 1e3 for a, b in evs])
 
 
 def _spin_cycles_per_ms():
@@ -155,11 +186,12 @@ def _spin_cycles_per_ms():
     return 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
 
 
-def kernel_durations(launchers, reps):
+def kernel_durations(launchers, reps, per_rep=False):
     """Per-launch GPU durations (us) of each callable, timed with HIP events on the
     current (launch) stream.  The launches are queued behind a spin kernel that
     outlasts the host's enqueue time, so host overhead cannot open idle gaps inside
-    a measured interval."""
+    a measured interval.  Returns the mean per callable, or with per_rep the list of
+    every repetition's duration per callable."""
     n = len(launchers)
     t0 = time.perf_counter()
     for fn in launchers:            # one unmeasured pass: host enqueue cost
@@ -178,8 +210,11 @@ def kernel_durations(launchers, reps):
             fn()
             b.record()
     torch.cuda.synchronize()
-    return [sum(evs[r][i][0].elapsed_time(evs[r][i][1]) for r in range(reps)) * 1e3 / reps
+    durs = [[evs[r][i][0].elapsed_time(evs[r][i][1]) * 1e3 for r in range(reps)]
             for i in range(n)]
+    if per_rep:
+        return durs
+    return [sum(d) / reps for d in durs]
 
 
 # ------------------------------------------------------------- workloads
@@ -213,8 +248,10 @@ def headline(skv, args):
     # dominant kernel: the single-launch decode kernel (all of the step's work);
     # durations per launch from HIP events.  The two-kernel form (partials, then
     # merge_state) is timed too, for comparison.
-    reps = max(5, min(args.steps, 20))
-    fused_us = kernel_durations([d.step for d in dec], reps)
+    reps = max(5, args.steps)
+    fused = [stats(x) for x in kernel_durations([d.step for d in dec], reps, per_rep=True)]
+    fused_us = [st["mean"] for st in fused]
+    step_st = time_graph(g, reps)
     launchers = []
     for d in dec:
         launchers += [d.partial, d.merge]
@@ -232,10 +269,12 @@ def headline(skv, args):
         gbs = d.step_bytes() / (us * 1e-6) / 1e9
         per[str(L)] = dict(num_splits=d.S, us=round(us, 2), gbs=round(gbs, 1),
                            frac=round(gbs / HBM_PEAK_GBS, 4),
+                           p10_us=round(fused[i]["p10"], 2), p50_us=round(fused[i]["p50"], 2),
+                           p90_us=round(fused[i]["p90"], 2),
                            two_kernel_us=round(part_us[i] + merge_us[i], 2),
                            partial_us=round(part_us[i], 2), merge_us=round(merge_us[i], 2))
     return dec, dict(ms=ms, value=value, step_bytes=step_bytes, achieved=achieved,
-                     avg_us=avg_us, avg_bytes=avg_bytes, per=per)
+                     avg_us=avg_us, avg_bytes=avg_bytes, per=per, step_st=step_st)
 
 
 def parity_sample(dec):
@@ -286,7 +325,12 @@ def cpu_baseline(dec, args):
 def secondary(skv, args, dec):
     import workloads as wl
     res = {}
-    reps = 20
+    reps = 50
+
+    def pct(st):
+        """Median (`us`) and spread of per-replay times, rounded."""
+        return dict(us=round(st["p50"], 2), p10_us=round(st["p10"], 2), p90_us=round(st["p90"], 2),
+                    mean_us=round(st["mean"], 2))
 
     # partly filled KV cache: the Lkv-32768 decode_gqa problem with every kv_len = 4096
     # (lengths on the device, split count chosen for the capacity, as a captured
@@ -299,11 +343,11 @@ def secondary(skv, args, dec):
     def partly_filled():
         skv.attn_splitkv_decode(d32.q, d32.k, d32.v, num_splits=d32.S, scale=d32.scale,
                                 out=d32.out, lse=d32.lse, workspace=d32.ws, kv_len=kvl)
-    us = kernel_durations([partly_filled], reps)[0]
+    st = stats(kernel_durations([partly_filled], reps, per_rep=True)[0])
+    us = st["p50"]
     fb = 2 * B * Hkv * filled * D * 2 + 2 * B * Hq * Lq * D * 2 + B * Hq * Lq * 4
     res["decode_gqa_capacity32768_kvlen4096"] = dict(
-        us=round(us, 2), gbs=round(fb / (us * 1e-6) / 1e9, 1), num_splits=d32.S,
-        filled_bytes=fb)
+        **pct(st), gbs=round(fb / (us * 1e-6) / 1e9, 1), num_splits=d32.S, filled_bytes=fb)
 
     # wide-head decode: B4 Hq16 Hkv4 Lq4 D256, K offset +2; the two problems
     # alternate, so each reads what the other evicted
@@ -312,13 +356,13 @@ def secondary(skv, args, dec):
         log(f"generating wide_decode Lkv={L}")
         wides.append((L, Decode(skv, wl.wide_decode(L, +1))))
     launchers = [d.step for _, d in wides]
-    durs = kernel_durations(launchers, reps)
+    durs = kernel_durations(launchers, reps, per_rep=True)
     for i, (L, d) in enumerate(wides):
-        us = durs[i]
+        st = stats(durs[i])
+        us = st["p50"]
         gbs = d.step_bytes() / (us * 1e-6) / 1e9
         res[f"decode_wide_D256_Lq4_Lkv{L}"] = dict(
-            us=round(us, 2), gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
-            num_splits=d.S)
+            **pct(st), gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4), num_splits=d.S)
     del wides, launchers
     torch.cuda.empty_cache()
 
@@ -333,11 +377,12 @@ def secondary(skv, args, dec):
 
     def varlen():
         skv.attn_fwd_varlen(q, k, v, cq, ck, mx, scale=vl.scale, causal=True, out=out, lse=lse)
-    us = time_graph(capture(varlen), reps)
+    st = time_graph(capture(varlen), reps)
+    us = st["p50"]
     fl = wl.prefill_flops(vl.lengths, 32, 128, causal=True)
     tf = fl / (us * 1e-6) / 1e12
     res["prefill_varlen_causal_16seq_Hq32_Hkv8_D128"] = dict(
-        us=round(us, 1), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4),
+        **pct(st), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4),
         total_tokens=vl.meta["T"], flop=fl)
     del q, k, v, out, lse
     torch.cuda.empty_cache()
@@ -366,9 +411,10 @@ def secondary(skv, args, dec):
     fl = 4 * 16 * 8192 * 8192 * 64
     for name, fn in (("prefill_ring_4chunks_smooth_merge_H16_S8192_D64_fp16", ring),
                      ("prefill_full_H16_S8192_D64_fp16", full)):
-        us = time_graph(capture(fn), reps)
+        st = time_graph(capture(fn), reps)
+        us = st["p50"]
         tf = fl / (us * 1e-6) / 1e12
-        res[name] = dict(us=round(us, 1), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4),
+        res[name] = dict(**pct(st), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4),
                          flop=fl)
     # INT8 QK^T with smoothing (fp16 P.V) on the same ring problem: per chunk + merge,
     # and unsplit.  Each call quantises its own q and chunk (mean(k), codes, scales),
@@ -388,9 +434,10 @@ def secondary(skv, args, dec):
         skv.sage_fwd(q, kf, vf, scale=rc["scale"], smooth_k=True, out=fo, lse=fl_, workspace=wsf)
     for name, fn in (("prefill_int8qk_ring_4chunks_smooth_merge_H16_S8192_D64_fp16", ring_int8),
                      ("prefill_int8qk_full_smooth_H16_S8192_D64_fp16", full_int8)):
-        us = time_graph(capture(fn), reps)
+        st = time_graph(capture(fn), reps)
+        us = st["p50"]
         tf = fl / (us * 1e-6) / 1e12
-        res[name] = dict(us=round(us, 1), tflops=round(tf, 1),
+        res[name] = dict(**pct(st), tflops=round(tf, 1),
                          frac_mfma_int8_fp16=round(tf / INT8_FP16_PEAK_TFLOPS, 4), flop=fl)
     del q, kc, vc, kf, vf, po, pl, mo, ml, fo, fl_, wsr, wsf
     torch.cuda.empty_cache()
@@ -411,14 +458,16 @@ def secondary(skv, args, dec):
     def dense8():
         skv.sage_fwd(q, k, v, scale=p.scale, smooth_k=True, out=out, lse=lse, workspace=wsd)
     fl = 4 * 32 * 8192 * 8192 * 128
-    us = time_graph(capture(dense16), reps)
+    st = time_graph(capture(dense16), reps)
+    us = st["p50"]
     tf = fl / (us * 1e-6) / 1e12
     res["prefill_dense_H32_Hkv8_S8192_D128_bf16"] = dict(
-        us=round(us, 1), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4), flop=fl)
-    us = time_graph(capture(dense8), reps)
+        **pct(st), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4), flop=fl)
+    st = time_graph(capture(dense8), reps)
+    us = st["p50"]
     tf = fl / (us * 1e-6) / 1e12
     res["prefill_int8qk_dense_smooth_H32_Hkv8_S8192_D128_bf16"] = dict(
-        us=round(us, 1), tflops=round(tf, 1),
+        **pct(st), tflops=round(tf, 1),
         frac_mfma_int8_fp16=round(tf / INT8_FP16_PEAK_TFLOPS, 4), flop=fl)
     del q, k, v, out, lse, wsd
     torch.cuda.empty_cache()
@@ -431,7 +480,7 @@ def secondary(skv, args, dec):
 
     def tiny():
         skv.attn_fwd(tq, tk, tv, scale=d["scale"], out=to, lse=tl)
-    res["tiny_lse_B1_H4_Sq64_Sk1000_D128"] = dict(us=round(time_graph(capture(tiny), reps), 2))
+    res["tiny_lse_B1_H4_Sq64_Sk1000_D128"] = pct(time_graph(capture(tiny), reps))
     return res
 
 
@@ -466,6 +515,17 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+def practical_ceilings():
+    """The practical ceilings of microbench/ceilings.hip, measured in this run (HBM read
+    stream with plain and with nontemporal loads, bf16 MFMA, LDS, exp/FMA rates), or
+    None when that library is not built."""
+    if not os.path.exists(os.path.join(ROOT, "microbench", "libceilings.so")):
+        return None
+    sys.path.insert(0, os.path.join(ROOT, "microbench"))
+    import ceilings
+    return {k: round(v, 1) for k, v in ceilings.measure().items()}
+
+
 def copy_probe():
     """A plain device copy of known size (256 MiB read + 256 MiB written), for
     scaling the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
@@ -492,6 +552,18 @@ def main():
         cpu = cpu_baseline(dec, args)
     sec = {} if args.no_secondary else secondary(skv, args, dec)
     copy_probe()
+    ceil = None if args.no_secondary else practical_ceilings()
+    if ceil:
+        # the same figures against the practical ceilings measured above
+        hbm = ceil["hbm_read_stream_nontemporal_GBs"]
+        mfma = ceil["mfma_bf16_32x32x16_tflops"]
+        for v in h["per"].values():
+            v["frac_practical"] = round(v["gbs"] / hbm, 4)
+        for v in sec.values():
+            if "gbs" in v:
+                v["frac_practical"] = round(v["gbs"] / hbm, 4)
+            if "frac_mfma" in v:
+                v["frac_mfma_practical"] = round(v["tflops"] / mfma, 4)
     line = {
         "metric": METRIC,
         "value": round(h["value"], 1),
@@ -524,11 +596,16 @@ def main():
             "kernel": "splitkv_kernel<bf16, 128, single-launch> (skv_attn_splitkv_decode)",
             "avg_launch_us": round(h["avg_us"], 2),
             "algorithmic_bytes_per_launch": int(h["avg_bytes"]),
+            "practical_peak": ceil["hbm_read_stream_nontemporal_GBs"] if ceil else None,
+            "frac_practical": (round(h["achieved"] / ceil["hbm_read_stream_nontemporal_GBs"], 4)
+                               if ceil else None),
         },
+        "step_us": {k: round(v, 2) for k, v in h["step_st"].items()},
         "cpu_baseline": cpu,
         "per_problem": h["per"],
         "parity_sample_max_err": round(err, 5),
         "secondary": sec,
+        "practical_ceilings": ceil,
     }
     print(json.dumps(line), flush=True)
 
