@@ -159,13 +159,15 @@ skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* 
  *   out  q's shape, layout and dtype: the merged output.
  *   lse  float32 [B, Hq, Lq] (log2) or NULL.
  *   workspace: device memory of skv_splitkv_workspace_bytes(B, Hq, Lq, D,
- *       num_splits, Hkv) bytes, 256-byte aligned, holding the partial states (chunk
- *       outputs in q's 16-bit type -- each is normalised by its own sum, so it lies in
- *       the range of V -- and float32 chunk LSEs) and one arrival counter per (batch,
- *       kv head).  It must be ZERO-FILLED before its
- *       first use; every call returns the counters to zero, so one zero fill serves
- *       any number of later calls (including HIP graph replays).  Two calls that
- *       may run at the same time must not share a workspace.
+ *       num_splits, Hkv) bytes, 256-byte aligned: a fixed block of arrival counters
+ *       at its start (one per (batch, kv head), room for 65536, the same bytes for
+ *       every shape), then the partial states (chunk outputs in q's 16-bit type --
+ *       each is normalised by its own sum, so it lies in the range of V -- and
+ *       float32 chunk LSEs).  It must be ZERO-FILLED before its first use; every call
+ *       returns its counters to zero, so one zero fill serves any number of later
+ *       calls of any shape that fits (including HIP graph replays).  Two calls that
+ *       may run at the same time must not share a workspace.  B*Hkv > 65536:
+ *       SKV_EUNSUPPORTED.
  */
 skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v, void* out,
                                      float* lse, int B, int Hq, int Hkv, int Lq, int Lkv, int D,

@@ -324,8 +324,9 @@ skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* 
 size_t skv_splitkv_workspace_bytes(int B, int Hq, int Lq, int D, int num_splits, int Hkv) {
     if (B <= 0 || Hq <= 0 || Lq <= 0 || D <= 0 || num_splits <= 0 || Hkv <= 0) return 0;
     const size_t rows = (size_t)num_splits * B * Hq * Lq;
-    return align256(rows * D * sizeof(uint16_t)) + align256(rows * sizeof(float)) +
-           align256((size_t)B * Hkv * sizeof(int));
+    // the counter block (fixed size, first), chunk outputs, chunk LSEs
+    return skv::kTicketBlockBytes + align256(rows * D * sizeof(uint16_t)) +
+           align256(rows * sizeof(float));
 }
 
 skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v, void* out,
@@ -344,6 +345,9 @@ skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v
     if (num_splits > skv::kMaxDecodeSplits)
         return fail(SKV_EUNSUPPORTED, "the single-launch decode takes at most %d splits (got %d)",
                     skv::kMaxDecodeSplits, num_splits);
+    if ((int64_t)B * Hkv > skv::kMaxDecodeUnits)
+        return fail(SKV_EUNSUPPORTED, "B*Hkv = %lld exceeds the %d arrival counters of the decode workspace",
+                    (long long)B * Hkv, skv::kMaxDecodeUnits);
     const size_t need = skv_splitkv_workspace_bytes(B, Hq, Lq, D, num_splits, Hkv);
     if (B > 0 && (!workspace || !aligned(workspace, 256)))
         return fail(SKV_EINVAL, "the decode workspace must be non-NULL and 256-byte aligned");
@@ -353,12 +357,13 @@ skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v
     const size_t rows = (size_t)num_splits * B * Hq * Lq;
     if (rows * D * sizeof(float) >= ((size_t)1 << 31))
         return fail(SKV_EUNSUPPORTED, "partial states exceed 2 GiB for the single-launch decode");
-    // chunk outputs in q's 16-bit type, chunk LSEs float32, one ticket per (batch, kv head)
+    // one ticket per (batch, kv head) in the fixed counter block, then the chunk
+    // outputs in q's 16-bit type and the float32 chunk LSEs
     char* ws = (char*)workspace;
     const size_t po_bytes = align256(rows * D * sizeof(uint16_t));
-    a.out_part = (float*)ws;
-    a.lse_part = (float*)(ws + po_bytes);
-    a.ticket = (int*)(ws + po_bytes + align256(rows * sizeof(float)));
+    a.ticket = (int*)ws;
+    a.out_part = (float*)(ws + skv::kTicketBlockBytes);
+    a.lse_part = (float*)(ws + skv::kTicketBlockBytes + po_bytes);
     a.out = out;
     a.lse = lse;
     return launched(skv::launch_splitkv(a, dtype, D, true, (hipStream_t)stream), "splitkv_decode");

@@ -121,6 +121,11 @@ hipError_t launch_fmha(const FmhaArgs& a, int dtype, int D, bool causal, bool va
 hipError_t launch_kmean(const KmeanArgs& a, int dtype, int D, bool varlen, int grid_b,
                         hipStream_t stream);
 constexpr int kMaxDecodeSplits = 256;  // single-launch decode: its merge walks S / 16 round trips
+// Single-launch decode: arrival counters for at most this many (batch, kv head) pairs,
+// in a block of fixed size at the start of the workspace, so that one zero fill serves
+// calls of any shape.
+constexpr int kMaxDecodeUnits = 65536;
+constexpr size_t kTicketBlockBytes = (size_t)kMaxDecodeUnits * sizeof(int);
 hipError_t launch_splitkv(const SplitArgs& a, int dtype, int D, bool fused, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int parts_dtype, int out_dtype, int D,
                         hipStream_t stream);

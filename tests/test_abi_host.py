@@ -202,10 +202,11 @@ def test_splitkv_decode_rejects(lib):
     assert call(wsb=16) == 1
     assert call(out=None) == 1
     assert call(B=0) == 0
+    assert call(B=8193, Hkv=8, Hq=8, ws=None, wsb=0) == 2   # B*Hkv over 65536 counters
     need = lib.skv_splitkv_workspace_bytes(2, 32, 1, 128, 8, 8)
     rows = 8 * 2 * 32
-    # 16-bit chunk outputs, float32 chunk LSEs, one int32 ticket per (batch, kv head)
-    assert need == ((rows * 128 * 2 + 255) // 256 + (rows * 4 + 255) // 256 + 1) * 256
+    # the fixed counter block (65536 int32), 16-bit chunk outputs, float32 chunk LSEs
+    assert need == 65536 * 4 + ((rows * 128 * 2 + 255) // 256 + (rows * 4 + 255) // 256) * 256
 
 
 def _sage_fwd(lib, **kw):

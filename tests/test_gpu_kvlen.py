@@ -109,10 +109,9 @@ def test_kv_len_single_launch_decode_nan_poisoned(skv, case):
     kv_len = torch.from_numpy(lens).to(DEV)
     ws = torch.zeros(skv.splitkv_workspace_bytes(B, Hq, Lq, D, S, Hkv), dtype=torch.uint8,
                      device=DEV)
-    # poison the partial-state part of the workspace (the counters must stay zero):
-    # all-ones bytes are NaN in float32 and in both 16-bit types
-    part_bytes = ws.numel() - ((B * Hkv * 4 + 255) // 256) * 256
-    ws[:part_bytes].fill_(0xFF)
+    # poison the partial-state part of the workspace (the counter block at its start
+    # must stay zero): all-ones bytes are NaN in float32 and in both 16-bit types
+    ws[65536 * 4:].fill_(0xFF)
     out = torch.full_like(q, float("nan"))
     lse = torch.full((B, Hq, Lq), float("nan"), dtype=torch.float32, device=DEV)
     skv.attn_splitkv_decode(q, k, v, num_splits=S, scale=p.scale, out=out, lse=lse,
