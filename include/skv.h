@@ -76,9 +76,10 @@ typedef enum { SKV_HND = 0, SKV_NHD = 1 } skv_layout_t;
  * call's Sk keys per (batch, kv head), and adds scale * q_i . mean(k) back into
  * the LSE, so the LSE still refers to the unsmoothed logits [ARK Problem
  * Description, second issue; Reproduction Steps part 3].  The output is
- * unchanged by smoothing.  It needs a float32 workspace of
- * skv_workspace_bytes(B, Hkv, D, 1) bytes (device memory, 16-byte aligned, no
- * initialisation required); without smoothing `workspace` may be NULL.
+ * unchanged by smoothing.  It needs a workspace of skv_workspace_bytes(B, Hkv, D, 1)
+ * bytes (device memory, 16-byte aligned, no initialisation required; it holds
+ * mean(k) and its partial sums, so calls that may run at the same time need separate
+ * workspaces); without smoothing `workspace` may be NULL.
  *
  * Sizes: B, Sq, Sk >= 0 (zero-sized problems return SKV_OK without launching,
  * except Sk == 0 with Sq > 0, which writes zero outputs and -inf LSEs).  Grid
