@@ -1,6 +1,6 @@
 """Benchmark of the split-KV decode step and the prefill forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--reps R]
 
 Headline workload: split-KV decode with GQA, B=8, Hq=32, Hkv=8, Lq=1, D=128, bf16,
 HND, with Lkv = 4096, 8192 and 32768.  One step runs the decode (split-KV partials
@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--reps", type=int, default=50,
+                    help="graph replays per secondary figure (default 50; fewer for profiled runs)")
     return ap.parse_args()
 
 
@@ -325,7 +327,7 @@ def cpu_baseline(dec, args):
 def secondary(skv, args, dec):
     import workloads as wl
     res = {}
-    reps = 50
+    reps = max(3, args.reps)
 
     def pct(st):
         """Median (`us`) and spread of per-replay times, rounded."""
