@@ -17,9 +17,10 @@
 //     max and sum live in that lane (plus its partner lane^32), and the LSE
 //     epilogue stores one value per row from one lane -- the per-row ownership the
 //     report's 16-row-block bug lacked.
-//   * Q stays in registers as the B operand for the whole key loop.  K and V tiles
-//     are staged global -> registers -> LDS (the next tile's loads are in flight
-//     while the current one is computed).
+//   * Q stays in registers as the B operand for the whole key loop; it arrives, and
+//     the output leaves, through a 32-row LDS slice per wave, so that global loads
+//     and stores cover whole rows.  K and V tiles are staged global -> registers ->
+//     LDS (the next tile's loads are in flight while the current one is computed).
 //   * The C layout of S^T is reused directly as the B operand of O^T += V^T P^T;
 //     the key order inside P is permuted and V^T is read from LDS with
 //     ds_read_b64_tr_b16 in the matching permuted order (a sum over keys does not
