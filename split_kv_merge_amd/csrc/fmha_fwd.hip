@@ -85,11 +85,14 @@ void fmha_fwd_kernel(FmhaArgs a) {
     // Grid (head, batch | sequence, row tile), dispatched head-fastest: with causal
     // masking the row tiles run last-first, so the work groups go out in order of
     // decreasing work (a row tile's key count grows with its index) across every
-    // head and sequence, and none of the long ones trails the grid.  Head-fastest
-    // also keeps each head's work groups on one XCD (work groups are dealt to the
-    // XCDs round-robin and Hq is normally a multiple of their count), so its K/V
-    // stays in one L2.
-    const int h = blockIdx.x, b = blockIdx.y;
+    // head and sequence, and none of the long ones trails the grid.  Work groups are
+    // dealt to the 8 XCDs round-robin, so head slot x lands on XCD x % 8; when Hq is
+    // a multiple of 8, XCD x takes the contiguous heads x Hq/8 .. (x + 1) Hq/8 - 1,
+    // and the query heads that share a K/V head (GQA) share one L2, where they read
+    // the same tiles at about the same time (varlen causal prefill: -2 %).
+    const int h = (a.Hq & 7) ? (int)blockIdx.x
+                             : (int)(blockIdx.x & 7) * (a.Hq >> 3) + (int)(blockIdx.x >> 3);
+    const int b = blockIdx.y;
     const int mt = CAUSAL ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
 
     int Lq, Lk;

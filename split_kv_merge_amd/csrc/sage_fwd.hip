@@ -76,8 +76,12 @@ void sage_fwd_kernel(SageFwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int n = lane & 31, hg = lane >> 5;
-    // grid (head, batch, row tile), head-fastest, causal row tiles last-first
-    const int h = blockIdx.x, b = blockIdx.y;
+    // grid (head, batch, row tile), head-fastest, causal row tiles last-first; with
+    // Hq a multiple of 8 each XCD takes a contiguous block of Hq/8 heads, so the query
+    // heads of one K/V head share an L2
+    const int h = (a.Hq & 7) ? (int)blockIdx.x
+                             : (int)(blockIdx.x & 7) * (a.Hq >> 3) + (int)(blockIdx.x >> 3);
+    const int b = blockIdx.y;
     const int mt = CAUSAL ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
     const int Lq = a.Sq, Lk = a.Sk;
     const int m0 = mt * BM;
