@@ -2,7 +2,7 @@
 fixed seed.
 
 The fixed-case tests pin chosen shapes (tile multiples, ragged tails, empty inputs);
-this sweep draws 24 more per entry point -- batch, head counts and grouping, query
+this sweep draws 64 more per entry point (32 for the varlen and INT8 calls) -- batch, head counts and grouping, query
 and key lengths from 1 to a few tiles past the tile size, head dimension, dtype,
 layout, causal masking, smoothing, key offsets, split counts, filled KV lengths --
 from numpy's default generator with seed 2026, so a shape class the chosen cases
@@ -21,7 +21,7 @@ from tests.tolerance import assert_lse_close, assert_out_close
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-N_CASES = 24
+N_CASES = 64
 
 
 @pytest.fixture(scope="module")
