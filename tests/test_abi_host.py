@@ -270,3 +270,27 @@ def test_sage_quant_rejects(lib):
     assert call(D=256) == 2
     assert call(Hkv=3) == 1
     assert call(B=0) == 0
+
+
+def _header_prototypes():
+    """name -> parameter count of every skv_* prototype in include/skv.h."""
+    import re
+    text = open(os.path.join(ROOT, "include", "skv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(skv_\w+)\s*\(([^;{]*?)\)\s*;", text):
+        params = " ".join(m.group(2).split())
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argtypes_match_the_header(lib):
+    """The ctypes binding declares, for every entry point, as many arguments as the
+    C prototype has: a drift would shift arguments into the wrong slots silently."""
+    import split_kv_merge_amd as skv
+    protos = _header_prototypes()
+    assert set(protos) == set(_declared())
+    for name, n in protos.items():
+        fn = getattr(skv._lib, name)
+        assert fn.argtypes is not None, f"{name}: no argtypes in the binding"
+        assert len(fn.argtypes) == n, f"{name}: binding {len(fn.argtypes)} args, header {n}"
