@@ -27,7 +27,8 @@
  *     key to read), contiguous in the named layout, with
  *     the head dimension D innermost; q/k/v/out must be 16-byte aligned, LSE
  *     buffers 4-byte aligned.  The caller owns every buffer; the library keeps no
- *     state, allocates nothing and never synchronises: each call only enqueues
+ *     state (apart from the fixed device scratch of skv_attn_splitkv_decode_noalloc),
+ *     allocates nothing and never synchronises: each call only enqueues
  *     kernels on `stream` (a hipStream_t; NULL = the default stream), so calls can
  *     be captured into a HIP graph.
  *   - Shapes are checked before anything is launched or written [SGL review:
@@ -178,6 +179,36 @@ skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v
 
 /* Workspace bytes of skv_attn_splitkv_decode (0 for non-positive sizes). */
 size_t skv_splitkv_workspace_bytes(int B, int Hq, int Lq, int D, int num_splits, int Hkv);
+
+/*
+ * The single-launch decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It computes exactly what skv_attn_splitkv_decode computes (the same kernels),
+ * but keeps its arrival counters and partial states in a fixed device scratch that
+ * the library holds, instead of a caller workspace; the caller still passes q, k,
+ * v, out and lse.  The call allocates nothing and calls no allocating routine.
+ *
+ *   Arguments, limits and results: as skv_attn_splitkv_decode without the workspace.
+ *   Scratch: skv_splitkv_decode_noalloc_max_bytes() bytes (16 MiB) per device,
+ *       taken on the first call on a device and held until the process ends.  A call
+ *       whose skv_splitkv_workspace_bytes(B, Hq, Lq, D, num_splits, Hkv) exceeds it
+ *       returns SKV_EUNSUPPORTED before any launch (a decode of 8 x 32 query rows at
+ *       D = 128 fits with up to 128 splits).
+ *   The first call on a device also enqueues one small kernel that zeroes the
+ *       counters; every call leaves them at zero again.
+ *   Concurrency: all calls on one device share that device's scratch, so calls that
+ *       may overlap on one GPU (other streams, other threads) race and give wrong
+ *       results; serialise them, or use skv_attn_splitkv_decode with one workspace
+ *       per concurrent call.
+ */
+skv_status_t skv_attn_splitkv_decode_noalloc(const void* q, const void* k, const void* v,
+                                             void* out, float* lse, int B, int Hq, int Hkv, int Lq,
+                                             int Lkv, int D, skv_dtype_t dtype,
+                                             skv_layout_t layout, float scale, int num_splits,
+                                             const int32_t* kv_len, void* stream);
+
+/* Bytes of the device scratch of skv_attn_splitkv_decode_noalloc (its size limit). */
+size_t skv_splitkv_decode_noalloc_max_bytes(void);
 
 /*
  * Stable merge of num_parts partial states (o_s, lse_s) per row [ET Copilot

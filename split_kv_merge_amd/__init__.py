@@ -9,8 +9,9 @@ fallback: if the library is missing, every call raises.
 
 Functions (same names as the C entry points without the ``skv_`` prefix):
     attn_fwd, attn_fwd_varlen, attn_splitkv_partial, attn_splitkv_decode,
-    merge_state, workspace_bytes, splitkv_workspace_bytes, pick_num_splits,
-    lse_varlen_to_dense, sage_quant, sage_fwd, sage_workspace_bytes
+    attn_splitkv_decode_noalloc, splitkv_decode_noalloc_max_bytes, merge_state,
+    workspace_bytes, splitkv_workspace_bytes, pick_num_splits, lse_varlen_to_dense,
+    sage_quant, sage_fwd, sage_workspace_bytes
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ import os
 import torch
 
 __all__ = ["attn_fwd", "attn_fwd_varlen", "attn_splitkv_partial", "attn_splitkv_decode",
+           "attn_splitkv_decode_noalloc", "splitkv_decode_noalloc_max_bytes",
            "merge_state", "workspace_bytes", "splitkv_workspace_bytes", "pick_num_splits",
            "lse_varlen_to_dense", "sage_quant", "sage_fwd", "sage_workspace_bytes", "SkvError",
            "lib_path"]
@@ -64,6 +66,10 @@ def _load():
     lib.skv_attn_splitkv_partial.restype = I
     lib.skv_attn_splitkv_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, SZ, P]
     lib.skv_attn_splitkv_decode.restype = I
+    lib.skv_attn_splitkv_decode_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P]
+    lib.skv_attn_splitkv_decode_noalloc.restype = I
+    lib.skv_splitkv_decode_noalloc_max_bytes.argtypes = []
+    lib.skv_splitkv_decode_noalloc_max_bytes.restype = SZ
     lib.skv_splitkv_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.skv_splitkv_workspace_bytes.restype = SZ
     lib.skv_merge_state.argtypes = [I, I, I, I, I, P, I, I64, I64P, P, I64, I64P, P, I, I64P, P, I64P, P]
@@ -329,6 +335,44 @@ def attn_splitkv_decode(q, k, v, num_splits=None, scale=None, layout="HND", out=
                                        Lq, Lkv, D, _dt(q), SKV_HND if layout == "HND" else SKV_NHD,
                                        float(scale), S, _ptr(kv_len), _ptr(workspace), ws_bytes,
                                        _stream(q.device)))
+    return (out, lse) if lse is not None else out
+
+
+def splitkv_decode_noalloc_max_bytes() -> int:
+    return int(_load().skv_splitkv_decode_noalloc_max_bytes())
+
+
+def attn_splitkv_decode_noalloc(q, k, v, out, lse=None, num_splits=None, scale=None,
+                                layout="HND", kv_len=None):
+    """The single-launch decode of ``attn_splitkv_decode`` with its partial states in
+    the library's fixed device scratch instead of a workspace: the call allocates
+    nothing, so ``out`` (q's shape and dtype) must be given, and ``lse`` (float32
+    [B, Hq, Lq]) too if wanted.  Calls that may overlap on one GPU share that scratch
+    and must not run at the same time.  Returns (out, lse), or out when lse is None."""
+    lib = _load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _need_cuda_contig(n, t)
+    if v.shape != k.shape or q.dtype != k.dtype or v.dtype != k.dtype:
+        raise ValueError("k and v must match in shape, and q, k, v in dtype")
+    B, Hq, Hkv, Lq, Lkv, D = _dims(q, k, layout)
+    if Hkv <= 0 or Hq % Hkv:
+        raise ValueError(f"Hq ({Hq}) must be a multiple of Hkv ({Hkv})")
+    _check_kv_len(kv_len, B)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    if lse is not None:
+        _need_cuda_contig("lse", lse)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Lq):
+            raise ValueError(f"lse must be float32 {(B, Hq, Lq)}")
+    if num_splits is None:
+        num_splits = pick_num_splits(B, Hkv, (Hq // Hkv) * Lq, Lkv, D)
+    if scale is None:
+        scale = D ** -0.5
+    _check(lib.skv_attn_splitkv_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B,
+                                               Hq, Hkv, Lq, Lkv, D, _dt(q),
+                                               SKV_HND if layout == "HND" else SKV_NHD,
+                                               float(scale), int(num_splits), _ptr(kv_len),
+                                               _stream(q.device)))
     return (out, lse) if lse is not None else out
 
 

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libskv.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 SOURCES = ["api.cpp", "fmha_fwd.hip", "splitkv.hip", "merge.hip", "kmean.hip",
-           "sage_quant.hip", "sage_fwd.hip"]
+           "sage_quant.hip", "sage_fwd.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 

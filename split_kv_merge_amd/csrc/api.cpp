@@ -329,14 +329,17 @@ size_t skv_splitkv_workspace_bytes(int B, int Hq, int Lq, int D, int num_splits,
            align256(rows * sizeof(float));
 }
 
-skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v, void* out,
-                                     float* lse, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
-                                     skv_dtype_t dtype, skv_layout_t layout, float scale,
-                                     int num_splits, const int32_t* kv_len, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
-    clear_err();
+}  // extern "C"
+
+namespace {
+
+// Checks of the single-launch decode that do not depend on where its partial states
+// live; on success `a` holds the launch arguments without the state pointers.
+skv_status_t prepare_decode(const void* q, const void* k, const void* v, void* out, float* lse,
+                            int B, int Hq, int Hkv, int Lq, int Lkv, int D, skv_dtype_t dtype,
+                            skv_layout_t layout, float scale, int num_splits,
+                            const int32_t* kv_len, skv::SplitArgs& a) {
     if (!out) return fail(SKV_EINVAL, "out must be non-NULL");
-    skv::SplitArgs a;
     skv_status_t st = prepare_split(q, k, v, B, Hq, Hkv, Lq, Lkv, D, dtype, layout, scale,
                                     num_splits, kv_len, a);
     if (st != SKV_OK) return st;
@@ -348,25 +351,77 @@ skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v
     if ((int64_t)B * Hkv > skv::kMaxDecodeUnits)
         return fail(SKV_EUNSUPPORTED, "B*Hkv = %lld exceeds the %d arrival counters of the decode workspace",
                     (long long)B * Hkv, skv::kMaxDecodeUnits);
+    const size_t rows = (size_t)num_splits * B * Hq * Lq;
+    if (rows * D * sizeof(float) >= ((size_t)1 << 31))
+        return fail(SKV_EUNSUPPORTED, "partial states exceed 2 GiB for the single-launch decode");
+    a.out = out;
+    a.lse = lse;
+    return SKV_OK;
+}
+
+// Launch the single-launch decode with its counters and partial states in `ws`
+// (the layout skv_splitkv_workspace_bytes describes).
+skv_status_t launch_decode(skv::SplitArgs& a, int D, skv_dtype_t dtype, void* ws_ptr,
+                           hipStream_t stream) {
+    // one ticket per (batch, kv head) in the fixed counter block, then the chunk
+    // outputs in q's 16-bit type and the float32 chunk LSEs
+    const size_t rows = (size_t)a.num_splits * a.B * a.Hq * a.Lq;
+    char* ws = (char*)ws_ptr;
+    const size_t po_bytes = align256(rows * D * sizeof(uint16_t));
+    a.ticket = (int*)ws;
+    a.out_part = (float*)(ws + skv::kTicketBlockBytes);
+    a.lse_part = (float*)(ws + skv::kTicketBlockBytes + po_bytes);
+    return launched(skv::launch_splitkv(a, dtype, D, true, stream), "splitkv_decode");
+}
+
+}  // namespace
+
+extern "C" {
+
+skv_status_t skv_attn_splitkv_decode(const void* q, const void* k, const void* v, void* out,
+                                     float* lse, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                                     skv_dtype_t dtype, skv_layout_t layout, float scale,
+                                     int num_splits, const int32_t* kv_len, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    clear_err();
+    skv::SplitArgs a;
+    skv_status_t st = prepare_decode(q, k, v, out, lse, B, Hq, Hkv, Lq, Lkv, D, dtype, layout,
+                                     scale, num_splits, kv_len, a);
+    if (st != SKV_OK) return st;
     const size_t need = skv_splitkv_workspace_bytes(B, Hq, Lq, D, num_splits, Hkv);
     if (B > 0 && (!workspace || !aligned(workspace, 256)))
         return fail(SKV_EINVAL, "the decode workspace must be non-NULL and 256-byte aligned");
     if (workspace_bytes < need)
         return fail(SKV_EINVAL, "workspace has %zu bytes, the decode needs %zu", workspace_bytes, need);
     if (B == 0) return SKV_OK;
-    const size_t rows = (size_t)num_splits * B * Hq * Lq;
-    if (rows * D * sizeof(float) >= ((size_t)1 << 31))
-        return fail(SKV_EUNSUPPORTED, "partial states exceed 2 GiB for the single-launch decode");
-    // one ticket per (batch, kv head) in the fixed counter block, then the chunk
-    // outputs in q's 16-bit type and the float32 chunk LSEs
-    char* ws = (char*)workspace;
-    const size_t po_bytes = align256(rows * D * sizeof(uint16_t));
-    a.ticket = (int*)ws;
-    a.out_part = (float*)(ws + skv::kTicketBlockBytes);
-    a.lse_part = (float*)(ws + skv::kTicketBlockBytes + po_bytes);
-    a.out = out;
-    a.lse = lse;
-    return launched(skv::launch_splitkv(a, dtype, D, true, (hipStream_t)stream), "splitkv_decode");
+    return launch_decode(a, D, dtype, workspace, (hipStream_t)stream);
+}
+
+size_t skv_splitkv_decode_noalloc_max_bytes(void) { return skv::kNoAllocScratchBytes; }
+
+skv_status_t skv_attn_splitkv_decode_noalloc(const void* q, const void* k, const void* v,
+                                             void* out, float* lse, int B, int Hq, int Hkv, int Lq,
+                                             int Lkv, int D, skv_dtype_t dtype,
+                                             skv_layout_t layout, float scale, int num_splits,
+                                             const int32_t* kv_len, void* stream) {
+    clear_err();
+    skv::SplitArgs a;
+    skv_status_t st = prepare_decode(q, k, v, out, lse, B, Hq, Hkv, Lq, Lkv, D, dtype, layout,
+                                     scale, num_splits, kv_len, a);
+    if (st != SKV_OK) return st;
+    const size_t need = skv_splitkv_workspace_bytes(B, Hq, Lq, D, num_splits, Hkv);
+    if (need > skv::kNoAllocScratchBytes)
+        return fail(SKV_EUNSUPPORTED,
+                    "the no-allocation decode needs %zu bytes of partial states and counters, over "
+                    "its fixed %zu-byte device scratch (use skv_attn_splitkv_decode with a workspace)",
+                    need, skv::kNoAllocScratchBytes);
+    if (B == 0) return SKV_OK;
+    hipStream_t s = (hipStream_t)stream;
+    void* ws = nullptr;
+    hipError_t e = skv::noalloc_scratch(&ws, s);
+    if (e != hipSuccess)
+        return fail(SKV_ELAUNCH, "device scratch set-up failed: %s", hipGetErrorString(e));
+    return launch_decode(a, D, dtype, ws, s);
 }
 
 skv_status_t skv_merge_state(int num_parts, int R0, int R1, int R2, int D,

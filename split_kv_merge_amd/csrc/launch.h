@@ -127,6 +127,11 @@ constexpr int kMaxDecodeSplits = 256;  // single-launch decode: its merge walks 
 constexpr int kMaxDecodeUnits = 65536;
 constexpr size_t kTicketBlockBytes = (size_t)kMaxDecodeUnits * sizeof(int);
 hipError_t launch_splitkv(const SplitArgs& a, int dtype, int D, bool fused, hipStream_t stream);
+// Device-resident scratch of the no-allocation decode (scratch.hip): counters then
+// partial states, 16 MiB per device.  noalloc_scratch() returns this device's address
+// of it (looked up once per device, counters zeroed on first use).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void** ptr, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int parts_dtype, int out_dtype, int D,
                         hipStream_t stream);
 

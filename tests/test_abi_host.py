@@ -209,6 +209,33 @@ def test_splitkv_decode_rejects(lib):
     assert need == 65536 * 4 + ((rows * 128 * 2 + 255) // 256 + (rows * 4 + 255) // 256) * 256
 
 
+def test_splitkv_decode_noalloc_rejects_before_touching_the_device(lib):
+    """The no-allocation decode validates like the workspace form and refuses a
+    problem whose partial states do not fit its fixed scratch, all before any device
+    call (so these run without a GPU)."""
+    P = FAKE
+    cap = lib.skv_splitkv_decode_noalloc_max_bytes()
+    assert cap == 16 << 20
+
+    def call(**kw):
+        a = dict(B=8, Hq=32, Hkv=8, Lq=1, Lkv=4096, D=128, S=8, out=P, kv_len=None)
+        a.update(kw)
+        return lib.skv_attn_splitkv_decode_noalloc(P, P, P, a["out"], None, a["B"], a["Hq"],
+                                                   a["Hkv"], a["Lq"], a["Lkv"], a["D"], 0, 0, 0.1,
+                                                   a["S"], a["kv_len"], None)
+    assert call(S=257) == 2
+    assert call(out=None) == 1
+    assert call(Hq=30) == 1
+    assert call(B=0) == 0
+    # a decode of 8 x 32 rows at D = 128 fits with up to 128 splits ...
+    assert lib.skv_splitkv_workspace_bytes(8, 32, 1, 128, 128, 8) <= cap
+    # ... a problem whose partial states exceed the scratch is refused with a message
+    big = dict(B=64, Hq=64, Hkv=8, Lq=1, D=256, S=64)
+    assert lib.skv_splitkv_workspace_bytes(64, 64, 1, 256, 64, 8) > cap
+    assert call(**big) == 2
+    assert b"scratch" in lib.skv_last_error()
+
+
 def _sage_fwd(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=128,
              dtype=0, layout=0, scale=0.1, causal=0, smooth=1, ws=ctypes.c_void_p(0x20000),
