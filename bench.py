@@ -476,7 +476,7 @@ def secondary(skv, args, dec):
 
     # tiny LSE case: B1 H4 Sq64 Sk1000 D128 bf16 (launch-bound)
     d = wl.tiny_lse()
-    tq, tk, tv = d["q_rows"].cuda(), d["k"].cuda(), d["v"].cuda()
+    tq, tk, tv = d["q_graded"].cuda(), d["k"].cuda(), d["v"].cuda()
     to = torch.empty_like(tq)
     tl = torch.empty((1, 4, 64), dtype=torch.float32, device="cuda")
 
@@ -492,8 +492,10 @@ KERNEL_SOURCES = [os.path.join(ROOT, "split_kv_merge_amd", "csrc", f)
 
 
 def kernel_source_sha():
-    """SHA-256 of the decode kernel's sources with comments and whitespace removed,
-    so that the counter record goes stale when the code changes, not its comments."""
+    """SHA-256 of the decode kernel's sources with comments and whitespace removed:
+    splitkv.hip, device.h and, of launch.h, only the decode's argument block
+    (struct SplitArgs), so that the counter record goes stale when the decode's code
+    changes, not its comments or other kernels' declarations."""
     import hashlib
     import re
     h = hashlib.sha256()
@@ -501,6 +503,9 @@ def kernel_source_sha():
         text = open(f, encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
+        if f.endswith("launch.h"):
+            m = re.search(r"struct SplitArgs\s*\{.*?\};", text, flags=re.S)
+            text = m.group(0) if m else text
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 

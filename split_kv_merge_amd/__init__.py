@@ -425,13 +425,20 @@ def merge_state(o_parts, lse_parts, out_dtype=None, out=None, lse=None, return_l
     return (out, lse) if lse is not None else out
 
 
-def lse_varlen_to_dense(lse: torch.Tensor, B: int, S: int) -> torch.Tensor:
-    """View a varlen LSE [H, B*S] of B equal-length sequences as the dense [B, H, S]
+def lse_varlen_to_dense(lse: torch.Tensor, B: int, S: int, cu_seqlens=None) -> torch.Tensor:
+    """View a varlen LSE [H, B*S] of B sequences of S tokens each as the dense [B, H, S]
     layout (SGLang PR #33840 review thread: reshape to (H, B, S), swap the first two
-    axes).  The shape is checked first; sequences of unequal length cannot be
-    expressed densely and are rejected."""
+    axes).  The shape is checked first.  The LSE alone cannot show where one sequence
+    ends, so only with ``cu_seqlens`` (the int32 [B + 1] boundaries the varlen call
+    used; a GPU tensor is copied to the host, which synchronises) are sequences of
+    unequal length detected and rejected; without it the caller vouches that every
+    sequence has S tokens."""
     if lse.dim() != 2 or lse.shape[1] != B * S:
         raise ValueError(f"expected a varlen LSE [H, {B}*{S}], got {tuple(lse.shape)}")
+    if cu_seqlens is not None:
+        cu = [int(x) for x in torch.as_tensor(cu_seqlens).cpu().tolist()]
+        if cu != [b * S for b in range(B + 1)]:
+            raise ValueError(f"cu_seqlens {cu} does not describe {B} sequences of {S} tokens")
     return lse.reshape(lse.shape[0], B, S).transpose(0, 1)
 
 

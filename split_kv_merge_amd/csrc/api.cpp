@@ -181,7 +181,8 @@ skv_status_t skv_attn_fwd(const void* q, const void* k, const void* v, void* out
     a.kv_batch = (int64_t)Hkv * Sk * D;
     a.lse_head = Sq;
     a.lse_batch = (int64_t)Hq * Sq;
-    a.scale_log2 = scale * 1.4426950408889634f;
+    a.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+    a.negate_q = scale < 0.f;
     if (smooth_k) {
         char* ws = (char*)workspace;
         st = run_kmean_into(k, (float*)ws, (double*)(ws + kbar_bytes((size_t)B * Hkv, D)), nullptr,
@@ -241,7 +242,8 @@ skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
     a.q_row = (int64_t)Hq * D; a.q_head = D; a.q_batch = 0;
     a.kv_row = (int64_t)Hkv * D; a.kv_head = D; a.kv_batch = 0;
     a.lse_head = total_q; a.lse_batch = 0;
-    a.scale_log2 = scale * 1.4426950408889634f;
+    a.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+    a.negate_q = scale < 0.f;
     if (smooth_k) {
         char* ws = (char*)workspace;
         st = run_kmean_into(k, (float*)ws, (double*)(ws + kbar_bytes((size_t)nseq * Hkv, D)),
@@ -641,7 +643,8 @@ skv_status_t skv_sage_fwd(const void* q, const void* k, const void* v, void* out
     f.out = out; f.lse = lse;
     f.Hq = Hq; f.Hkv = Hkv; f.Sq = Sq; f.Sk = Sk;
     f.o_row = a.x_row[0]; f.o_head = a.x_head[0]; f.o_batch = a.x_batch[0];
-    f.scale_log2 = scale_log2;
+    f.scale_log2 = std::fabs(scale_log2);
+    f.negate_q = scale < 0.f;
     return launched(skv::launch_sage_fwd(f, dtype, D, causal != 0, grid_m, B, s), "sage_fwd");
 }
 

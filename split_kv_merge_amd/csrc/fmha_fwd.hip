@@ -207,9 +207,13 @@ void fmha_fwd_kernel(FmhaArgs a) {
     // read back from the slice (a wave's LDS accesses complete in order).
 #pragma unroll
     for (int c = 0; c < QCH; ++c) store16(qsl + c * RPC * QLD, qraw[c]);
+    // With a negative scale the operand is -q (a sign flip per element, exact) and the
+    // logit scale |scale|, so the raw dot products keep the order of the logits.
+    const uint32_t qsign = a.negate_q ? 0x80008000u : 0u;
     V8 qf[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_vec8<T>(load16(&qs[n * QLD + hg * (D / 2) + kk * 8]));
+    for (int kk = 0; kk < NKK; ++kk)
+        qf[kk] = as_vec8<T>(load16(&qs[n * QLD + hg * (D / 2) + kk * 8]) ^ qsign);
 
     // Smoothing bias in log2 units: scale*log2(e) * (q_row . mean(k)).
     float bias = 0.f;
@@ -322,7 +326,12 @@ void fmha_fwd_kernel(FmhaArgs a) {
             // p = 2^(s*c - bias - m_ref), packed to 16-bit as the B operand of PV.  The
             // row sum adds the packed (rounded) pairs with one dot2 against (1, 1): the
             // normaliser then sums exactly the P values the PV product uses.  Four
-            // partial sums keep the dependent chains short.
+            // partial sums keep the dependent chains short.  In masked tiles a masked
+            // logit gives p = 0 also when c = 0 (scale 0: every visible logit is 0).
+            auto logit = [&](float x) {
+                const float y = fmaf(x, c, nb);
+                return (MASK && x == -INFINITY) ? -INFINITY : y;
+            };
             uint32_t pk[NJB][2][4];
             float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -331,8 +340,8 @@ void fmha_fwd_kernel(FmhaArgs a) {
                 for (int st = 0; st < 2; ++st)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float p0 = fast_exp2(fmaf(s[jb][8 * st + 2 * j], c, nb));
-                        const float p1 = fast_exp2(fmaf(s[jb][8 * st + 2 * j + 1], c, nb));
+                        const float p0 = fast_exp2(logit(s[jb][8 * st + 2 * j]));
+                        const float p1 = fast_exp2(logit(s[jb][8 * st + 2 * j + 1]));
                         pk[jb][st][j] = E::pack2(p0, p1);
                         psum[j] = E::sum2(pk[jb][st][j], psum[j]);
                     }

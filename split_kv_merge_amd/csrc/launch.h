@@ -22,7 +22,11 @@ struct FmhaArgs {
     int64_t q_row, q_head, q_batch;     // q and out share strides
     int64_t kv_row, kv_head, kv_batch;  // k and v share strides
     int64_t lse_head, lse_batch;        // lse row stride is 1
-    float scale_log2;           // scale * log2(e)
+    // |scale| * log2(e); for a negative scale the kernel negates q (exactly) instead,
+    // so that every logit is taken as (-q) . k * |scale|: the max over raw dot
+    // products is then the max of the scaled logits for either sign of the scale
+    float scale_log2;
+    int negate_q;
 };
 
 // mean(k) over keys per (batch | sequence, kv head): float32 [B | nseq, Hkv, D].
@@ -108,7 +112,8 @@ struct SageFwdArgs {
     int Hq, Hkv, Sq, Sk;
     int64_t v_row, v_head, v_batch;
     int64_t o_row, o_head, o_batch;
-    float scale_log2;
+    float scale_log2;           // |scale| * log2(e); q's codes are negated when negate_q
+    int negate_q;
 };
 
 int sage_rows_per_block();     // query rows of one INT8 attention work group

@@ -118,10 +118,23 @@ void sage_fwd_kernel(SageFwdArgs a) {
     }
     // Q codes as the B operand: lane holds q^[row][hg*D/2 + 16kk .. +16) per k-step
     // (a wave's LDS accesses complete in order).
+    // With a negative scale the operand is -q^ (codes lie in [-127, 127], so each
+    // byte negates exactly) and the logit scale |scale|: the raw integer dot products
+    // keep the order of the logits.
     i32x4 qf[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-        qf[kk] = __builtin_bit_cast(i32x4, load16(qsb + n * KLD + hg * (D / 2) + kk * 16));
+    for (int kk = 0; kk < NKK; ++kk) {
+        u32x4 w = load16(qsb + n * KLD + hg * (D / 2) + kk * 16);
+        if (a.negate_q) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // bytewise 0 - x: ~x + 1 per byte, the carry kept inside each byte
+                const uint32_t nx = ~w[e];
+                w[e] = ((nx & 0x7f7f7f7fu) + 0x01010101u) ^ (nx & 0x80808080u);
+            }
+        }
+        qf[kk] = __builtin_bit_cast(i32x4, w);
+    }
     const float cq = wrow0 < Lq ? a.scale_log2 * a.q_scale[bh * nq + wrow0 / 32] : 0.f;
     const float bias = (a.q_bias && row_ok) ? a.q_bias[bh * Lq + row] : 0.f;
 
@@ -248,7 +261,8 @@ void sage_fwd_kernel(SageFwdArgs a) {
                 float mj = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mj = fmaxf(mj, s[jb][i]);
-                mx = fmaxf(mx, (mj - kMagicF) * cj[jb]);
+                // (c_j = 0 for an all-zero K block: its logits are 0, not NaN)
+                mx = fmaxf(mx, mj == -INFINITY ? -INFINITY : (mj - kMagicF) * cj[jb]);
             }
             mx = fmaxf(mx, xor_shfl(mx, 32));
             // (the codes are of k - mean(k): these logits are already the smoothed ones)
@@ -272,8 +286,16 @@ void sage_fwd_kernel(SageFwdArgs a) {
                 for (int st = 0; st < 2; ++st)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float p0 = fast_exp2(fmaf(s[jb][8 * st + 2 * j], cj[jb], nb));
-                        const float p1 = fast_exp2(fmaf(s[jb][8 * st + 2 * j + 1], cj[jb], nb));
+                        // masked logits give p = 0 also when c_j = 0 (an all-zero K
+                        // block, or scale 0)
+                        const float x0 = s[jb][8 * st + 2 * j], x1 = s[jb][8 * st + 2 * j + 1];
+                        float y0 = fmaf(x0, cj[jb], nb), y1 = fmaf(x1, cj[jb], nb);
+                        if (MASK) {
+                            y0 = x0 == -INFINITY ? -INFINITY : y0;
+                            y1 = x1 == -INFINITY ? -INFINITY : y1;
+                        }
+                        const float p0 = fast_exp2(y0);
+                        const float p1 = fast_exp2(y1);
                         pk[jb][st][j] = EV::pack2(p0, p1);
                         psum[j] = EV::sum2(pk[jb][st][j], psum[j]);
                     }

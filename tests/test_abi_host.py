@@ -182,6 +182,11 @@ def test_lse_varlen_to_dense_checks_shape():
     assert dense[1, 0, 1] == lse[0, 3]
     with pytest.raises(ValueError):
         skv.lse_varlen_to_dense(lse, 4, 2)
+    # with the boundaries, equal lengths pass and unequal ones (same total) are refused
+    cu_eq = torch.tensor([0, 2, 4, 6], dtype=torch.int32)
+    assert torch.equal(skv.lse_varlen_to_dense(lse, 3, 2, cu_seqlens=cu_eq), dense)
+    with pytest.raises(ValueError):
+        skv.lse_varlen_to_dense(lse, 3, 2, cu_seqlens=torch.tensor([0, 1, 4, 6], dtype=torch.int32))
 
 
 def test_splitkv_decode_rejects(lib):

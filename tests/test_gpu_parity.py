@@ -63,8 +63,8 @@ def test_tiny_lse_per_row(skv, dtype, layout, regime, smooth_k):
     """B1 H4 Sq64 Sk1000 D128: each q row scaled by linspace(0.25, 4), the 16-equal-row
     control, and K + 0.5; one LSE per row against the oracle, smoothing on and off."""
     d = wl.tiny_lse(seed=0, dtype=dtype)
-    q = d["q_rows"] if regime == "rows" else d["q_blocks"]
-    k = d["k_off"] if regime == "blocks_koff" else d["k"]
+    q = d["q_graded"] if regime == "rows" else d["q_grouped"]
+    k = d["k_shifted"] if regime == "blocks_koff" else d["k"]
     v = d["v"]
     if layout == "NHD":
         q, k, v = (wl.hnd_to_nhd(t) for t in (q, k, v))

@@ -123,17 +123,17 @@ def test_pages_workload_against_exact_attention(skv):
     within the INT8 error the ARK report prints for this workload (0.051 at most)
     of the exact LSE of the unsmoothed logits."""
     d = wl.tiny_lse(seed=0)
-    for qn in ("q_rows", "q_blocks"):
-        for kn in ("k", "k_off"):
+    for qn in ("q_graded", "q_grouped"):
+        for kn in ("k", "k_shifted"):
             for smooth in (True, False):
                 p = wl.Attn(d[qn], d[kn], d["v"], "HND", d["scale"])
                 o, l = _run(skv, p, False, smooth)
                 _, exact = oracle.attn(wl.bits(d[qn]), wl.bits(d[kn]), wl.bits(d["v"]), "bf16",
                                        scale=d["scale"])
                 err = np.abs(l - exact).max()
-                lim = 0.051 if qn == "q_blocks" else 0.15
+                lim = 0.051 if qn == "q_grouped" else 0.15
                 assert err <= lim, (qn, kn, smooth, err)
-                if qn == "q_rows":
+                if qn == "q_graded":
                     assert len(np.unique(l[0, 0])) == l.shape[2]
 
 

@@ -35,8 +35,8 @@ def test_tiny_lse_shape(skv, seed):
     """B1 H4 Sq64 Sk1000 D128 bf16, rows of distinct magnitude, K + 0.5, smooth_k on
     and off, HND and NHD."""
     d = wl.tiny_lse(seed=seed)
-    for qn, kn, smooth, layout in (("q_rows", "k", False, "HND"), ("q_rows", "k_off", True, "HND"),
-                                   ("q_blocks", "k_off", True, "NHD")):
+    for qn, kn, smooth, layout in (("q_graded", "k", False, "HND"), ("q_graded", "k_shifted", True, "HND"),
+                                   ("q_grouped", "k_shifted", True, "NHD")):
         q, k, v = d[qn], d[kn], d["v"]
         if layout == "NHD":
             q, k, v = wl.hnd_to_nhd(q), wl.hnd_to_nhd(k), wl.hnd_to_nhd(v)

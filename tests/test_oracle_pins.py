@@ -149,9 +149,9 @@ def test_matches_torch_float64_logsumexp_and_softmax():
     """The reproduction's reference formula, natural logsumexp / ln 2, evaluated by
     torch in float64 on the config-1 inputs; out by torch softmax(S) @ V."""
     d = wl.tiny_lse()
-    out, lse = oracle.attn(wl.bits(d["q_rows"]), wl.bits(d["k"]), wl.bits(d["v"]), "bf16",
+    out, lse = oracle.attn(wl.bits(d["q_graded"]), wl.bits(d["k"]), wl.bits(d["v"]), "bf16",
                            scale=d["scale"])
-    q, k, v = (d[n].to(torch.float64) for n in ("q_rows", "k", "v"))
+    q, k, v = (d[n].to(torch.float64) for n in ("q_graded", "k", "v"))
     s = (q @ k.transpose(-1, -2)) * d["scale"]
     ref_lse = (torch.logsumexp(s, dim=-1) / LN2).numpy()
     ref_out = (torch.softmax(s, dim=-1) @ v).numpy()
@@ -185,13 +185,13 @@ def _block_mutant(lse):
 
 def test_rows_get_distinct_lse_and_block_mutant_fails():
     d = wl.tiny_lse()
-    _, lse = oracle.attn(wl.bits(d["q_rows"]), wl.bits(d["k"]), wl.bits(d["v"]), "bf16")
+    _, lse = oracle.attn(wl.bits(d["q_graded"]), wl.bits(d["k"]), wl.bits(d["v"]), "bf16")
     assert len(np.unique(np.round(lse, 9))) == lse.size          # 256 distinct rows
     # The mutant must fail the parity bar by far (the report measured about 9 log2 units).
     assert lse_errors(_block_mutant(lse), lse) > 3.0
     # With 16 equal rows per block the mutant is invisible (the report's 0.000 column),
     # which is why inputs with distinct rows are required.
-    _, lse_b = oracle.attn(wl.bits(d["q_blocks"]), wl.bits(d["k"]), wl.bits(d["v"]), "bf16")
+    _, lse_b = oracle.attn(wl.bits(d["q_grouped"]), wl.bits(d["k"]), wl.bits(d["v"]), "bf16")
     assert lse_errors(_block_mutant(lse_b), lse_b) == 0.0
 
 
@@ -204,7 +204,7 @@ def test_lse_magnitudes_match_the_printed_reference_column():
     g = json.load(open(os.path.join(GOLDEN, "p1_error_logs.json")))
     rows = g["rows"]
     d = wl.tiny_lse(seed=0)
-    _, lse = oracle.attn(wl.bits(d["q_rows"]), wl.bits(d["k"]), wl.bits(d["v"]), "bf16")
+    _, lse = oracle.attn(wl.bits(d["q_graded"]), wl.bits(d["k"]), wl.bits(d["v"]), "bf16")
     got = lse[0, 0, rows]
     ref = np.array(g["reference_lse_log2"])
     assert abs(got.mean() - ref.mean()) < 0.3
@@ -217,8 +217,8 @@ def test_lse_magnitudes_match_the_printed_reference_column():
 
 def test_kmean_matches_numpy_mean():
     d = wl.tiny_lse()
-    km = oracle.kmean(wl.bits(d["k_off"]), "bf16")
-    assert np.allclose(km, _dec(d["k_off"]).mean(axis=2), rtol=0, atol=1e-14)
+    km = oracle.kmean(wl.bits(d["k_shifted"]), "bf16")
+    assert np.allclose(km, _dec(d["k_shifted"]).mean(axis=2), rtol=0, atol=1e-14)
 
 
 @pytest.mark.parametrize("layout", ["HND", "NHD"])
@@ -226,13 +226,13 @@ def test_smoothing_add_back_identity(layout):
     """LSE2(q, k) = LSE2(q, k - kbar) + scale * (q . kbar) / ln 2 exactly (the
     reproduction's part 3), and the outputs agree (softmax is shift-invariant)."""
     d = wl.tiny_lse()
-    q, k, v = d["q_blocks"], d["k_off"], d["v"]
+    q, k, v = d["q_grouped"], d["k_shifted"], d["v"]
     if layout == "NHD":
         q, k, v = (wl.hnd_to_nhd(t) for t in (q, k, v))
     kb = oracle.kmean(wl.bits(k), "bf16", layout)
     out, lse = oracle.attn(wl.bits(q), wl.bits(k), wl.bits(v), "bf16", layout)
     out_s, lse_s = oracle.attn(wl.bits(q), wl.bits(k), wl.bits(v), "bf16", layout, smoothed=True)
-    qd = _dec(d["q_blocks"])
+    qd = _dec(d["q_grouped"])
     shift = d["scale"] * np.einsum("bhsd,bhd->bhs", qd, kb) / LN2
     assert np.abs(lse - (lse_s + shift)).max() < 1e-10
     assert np.abs(out - out_s).max() < 1e-12

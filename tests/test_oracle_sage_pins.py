@@ -193,15 +193,15 @@ def test_logits_lse_and_out_within_quantisation_bound(smooth, offset, dtype):
 
 # ------------------------------------------------- the pages' workload and offsets
 
-@pytest.mark.parametrize("which,smooth", [("k", True), ("k", False), ("k_off", True),
-                                          ("k_off", False)])
+@pytest.mark.parametrize("which,smooth", [("k", True), ("k", False), ("k_shifted", True),
+                                          ("k_shifted", False)])
 def test_int8_lse_error_on_the_pages_workload(which, smooth):
     """B1 H4 Sq64 Sk1000 D128 bf16 with 16 equal rows per block: the ARK report's
     table prints INT8 QK^T LSE errors of 0.022 (smooth_k off), 0.051 (smooth_k off,
     K + 0.5) and 0.032 (smooth_k on, K + 0.5, after adding the shift back).  This
     reading, on the same workload, stays within the largest of them."""
     d = wl.tiny_lse(seed=0)
-    qb, kb, vb = wl.bits(d["q_blocks"]), wl.bits(d[which]), wl.bits(d["v"])
+    qb, kb, vb = wl.bits(d["q_grouped"]), wl.bits(d[which]), wl.bits(d["v"])
     _, rl = oracle.attn(qb, kb, vb, "bf16")
     _, sl = oracle.sage_attn(qb, kb, vb, "bf16", smooth_k=smooth)
     err = np.abs(sl - rl).max()

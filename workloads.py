@@ -64,13 +64,13 @@ class Attn:
 
 
 def attn_problem(B, Hq, Hkv, Sq, Sk, D, dtype="bf16", layout="HND", seed=0,
-                 row_scale=(0.25, 4.0), k_offset=0.0, q_mul=1.0, causal=False) -> Attn:
-    """Generic problem: q/k/v ~ N(0,1); each q row times U(row_scale) (one scalar per
-    (b, h, row)), times q_mul; k + k_offset; all in fp32 before one rounding."""
+                 q_mag=(0.25, 4.0), k_offset=0.0, q_mul=1.0, causal=False) -> Attn:
+    """Generic problem: q/k/v ~ N(0,1); each q row times a magnitude ~ U(q_mag) (one
+    scalar per (b, h, row)), times q_mul; k + k_offset; all in fp32 before one rounding."""
     g = torch.Generator().manual_seed(seed)
     q = torch.randn(B, Hq, Sq, D, generator=g)
-    if row_scale is not None:
-        lo, hi = row_scale
+    if q_mag is not None:
+        lo, hi = q_mag
         q = q * (lo + (hi - lo) * torch.rand(B, Hq, Sq, 1, generator=g))
     q = _to(q * q_mul, dtype)
     k = _to(torch.randn(B, Hkv, Sk, D, generator=g) + k_offset, dtype)
@@ -78,29 +78,32 @@ def attn_problem(B, Hq, Hkv, Sq, Sk, D, dtype="bf16", layout="HND", seed=0,
     if layout == "NHD":
         q, k, v = hnd_to_nhd(q), hnd_to_nhd(k), hnd_to_nhd(v)
     return Attn(q, k, v, layout, default_scale(D), causal,
-                dict(seed=seed, row_scale=row_scale, k_offset=k_offset, q_mul=q_mul))
+                dict(seed=seed, q_mag=q_mag, k_offset=k_offset, q_mul=q_mul))
 
 
 # ------------------------------------------------------------------ config 1
 
 def tiny_lse(seed=0, dtype="bf16"):
-    """B=1, H=4, Sq=64, Sk=1000, D=128, HND, scale D**-0.5.
+    """Config 1, the shape of the ARK return_lse report (auto-round #2556, Reproduction
+    Steps): batch 1, 4 heads, 64 queries, 1000 keys, head dim 128, HND, scale D**-0.5.
 
-    Returns dict with q, k, v, q_rows (row i times linspace(0.25, 4, 64)[i]),
-    q_blocks (every 16th row of q_rows repeated 16 times) and k_off (k + 0.5),
-    the three regimes of the ARK return_lse bug report's reproduction.
+    Draws q, k, v ~ N(0,1) (in that order, each rounded once) and derives three inputs
+    from them: ``q_graded``, whose query row i carries the magnitude 0.25 + 3.75 i / 63
+    (evenly spaced from 0.25 to 4), so every row has its own LSE; ``q_grouped``, where
+    each group of 16 consecutive rows repeats the group's first graded row, the control
+    in which a 16-row-block LSE bug is invisible; and ``k_shifted`` = k + 0.5, a common
+    key offset that smoothing must absorb.
     """
-    B, H, SQ, SK, D = 1, 4, 64, 1000, 128
-    g = torch.Generator().manual_seed(seed)
-    q = _to(torch.randn(B, H, SQ, D, generator=g), dtype)
-    k = _to(torch.randn(B, H, SK, D, generator=g), dtype)
-    v = _to(torch.randn(B, H, SK, D, generator=g), dtype)
-    row_scale = torch.linspace(0.25, 4.0, SQ).view(1, 1, SQ, 1)
-    q_rows = _to(q.float() * row_scale, dtype)
-    q_blocks = q_rows[:, :, ::16].repeat_interleave(16, dim=2).contiguous()
-    k_off = _to(k.float() + 0.5, dtype)
-    return dict(q=q, k=k, v=v, q_rows=q_rows, q_blocks=q_blocks, k_off=k_off,
-                scale=default_scale(D), B=B, H=H, Sq=SQ, Sk=SK, D=D, seed=seed)
+    n_q, n_k, d = 64, 1000, 128
+    gen = torch.Generator().manual_seed(seed)
+    q, k, v = (_to(torch.randn(1, 4, n, d, generator=gen), dtype) for n in (n_q, n_k, n_k))
+    magnitude = torch.linspace(0.25, 4.0, n_q)
+    graded = _to(q.float() * magnitude[:, None], dtype)
+    group_lead = (torch.arange(n_q) // 16) * 16
+    grouped = graded.index_select(2, group_lead)
+    shifted = _to(k.float() + 0.5, dtype)
+    return dict(q=q, k=k, v=v, q_graded=graded, q_grouped=grouped, k_shifted=shifted,
+                scale=default_scale(d), B=1, H=4, Sq=n_q, Sk=n_k, D=d, seed=seed)
 
 
 # ------------------------------------------------------------------ config 2
