@@ -1,12 +1,13 @@
 """GPU parity at the measured sizes, in the launch configuration bench.py times.
 
-The oracle cannot finish these problems whole in seconds, so each test runs the
-full problem on the GPU and compares a seeded sample of query rows (always
-including the first and last row of every batch element or sequence) with the
-oracle's per-row attention.  Every row of the output is also checked for what
-holds at any size: it is finite (each row here sees at least one key), and for
-decode it lies inside the per-column range of V over the keys its head reads (a
-softmax average of V's rows cannot leave that range).
+Decode problems have 256 query rows: the oracle computes every one (about a second
+each), and every row is compared.  The prefill problems are too large for the oracle
+whole, so they compare a seeded sample of query rows (always including the first and
+last row of every batch element or sequence) with the oracle's per-row attention.
+Every row of the output is also checked for what holds at any size: it is finite
+(each row here sees at least one key), and for decode it lies inside the per-column
+range of V over the keys its head reads (a softmax average of V's rows cannot leave
+that range).
 """
 from __future__ import annotations
 
@@ -40,17 +41,26 @@ def _sample_rows(B, H, L, n, seed):
     return np.array(sorted(set(rows)), np.int64)
 
 
-def _decode_full(skv, p, n_rows, seed):
+_PROBLEMS = {}
+
+
+def _decode_problem(kind, *key):
+    """Generated once per module: (problem, oracle out, oracle lse) of a full-size decode
+    problem; the oracle runs over every query row (256 rows per problem)."""
+    if (kind,) + key not in _PROBLEMS:
+        p = wl.decode_gqa(*key) if kind == "gqa" else wl.wide_decode(*key)
+        ro, rl = oracle.attn(wl.bits(p.q), wl.bits(p.k), wl.bits(p.v), "bf16", scale=p.scale)
+        _PROBLEMS.clear()            # keep one problem's tensors alive at a time
+        _PROBLEMS[(kind,) + key] = (p, ro, rl)
+    return _PROBLEMS[(kind,) + key]
+
+
+def _check_decode_rows(p, out, lse, ro, rl):
+    """Every row against the oracle, plus the range property: a softmax average of V's
+    rows stays inside the per-column range of V over the keys its head reads."""
     B, Hq, Hkv, Lq, Lkv, D = p.dims
     G = Hq // Hkv
-    S = skv.pick_num_splits(B, Hkv, G * Lq, Lkv, D)
-    q, k, v = p.q.to(DEV), p.k.to(DEV), p.v.to(DEV)
-    out = torch.full_like(q, float("nan"))
-    lse = torch.full((B, Hq, Lq), float("nan"), dtype=torch.float32, device=DEV)
-    ws = torch.zeros(skv.splitkv_workspace_bytes(B, Hq, Lq, D, S, Hkv), dtype=torch.uint8,
-                     device=DEV)
-    skv.attn_splitkv_decode(q, k, v, num_splits=S, scale=p.scale, out=out, lse=lse, workspace=ws)
-    # per-column V range over the keys of each kv head, broadcast to its query heads
+    v = p.v.to(DEV)
     vmin = v.float().amin(dim=2).repeat_interleave(G, dim=1)[:, :, None, :]
     vmax = v.float().amax(dim=2).repeat_interleave(G, dim=1)[:, :, None, :]
     torch.cuda.synchronize()
@@ -58,33 +68,63 @@ def _decode_full(skv, p, n_rows, seed):
     assert torch.isfinite(lse).all() and torch.isfinite(o).all()
     slack = 1e-2 + 1e-2 * torch.maximum(vmin.abs(), vmax.abs())
     assert ((o >= vmin - slack) & (o <= vmax + slack)).all()
-
-    rows = _sample_rows(B, Hq, Lq, n_rows, seed)
-    ro, rl = oracle.attn_rows(wl.bits(p.q), wl.bits(p.k), wl.bits(p.v), "bf16", rows,
-                              scale=p.scale)
-    o_c, l_c = o.cpu().numpy(), lse.cpu().numpy()
-    got_o = np.stack([o_c[b, h, i] for b, h, i in rows])
-    got_l = np.array([l_c[b, h, i] for b, h, i in rows])
-    assert_lse_close(got_l, rl)
-    assert_out_close(got_o, ro)
-    return S
+    assert_lse_close(lse.cpu(), rl)
+    assert_out_close(o.cpu(), ro)
 
 
+def _single_launch(skv, p, S):
+    B, Hq, Hkv, Lq, Lkv, D = p.dims
+    q, k, v = p.q.to(DEV), p.k.to(DEV), p.v.to(DEV)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, Hq, Lq), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(skv.splitkv_workspace_bytes(B, Hq, Lq, D, S, Hkv), dtype=torch.uint8,
+                     device=DEV)
+    skv.attn_splitkv_decode(q, k, v, num_splits=S, scale=p.scale, out=out, lse=lse, workspace=ws)
+    return out, lse
+
+
+@pytest.mark.parametrize("S", [0, 8, 16, 32])
 @pytest.mark.parametrize("Lkv", [4096, 8192, 32768])
-def test_decode_gqa_full_size(skv, Lkv):
-    """B8 Hq32 Hkv8 Lq1 D128 bf16 decode, the split count pick_num_splits chooses,
-    one launch (partials + in-kernel merge)."""
-    p = wl.decode_gqa(Lkv)
-    S = _decode_full(skv, p, n_rows=48, seed=Lkv)
-    assert S >= 1
+def test_decode_gqa_full_size(skv, Lkv, S):
+    """B8 Hq32 Hkv8 Lq1 D128 bf16 decode, all 256 rows against the oracle.
+
+    S = 0: the split count pick_num_splits chooses, in one launch (partials + in-kernel
+    merge), as bench.py times it.  S = 8, 16, 32: config 2 as written, the keys split
+    into S chunks: every chunk's partial (out, LSE) against the oracle's partial of that
+    chunk, their merge_state against the oracle's unsplit run, and the single-launch
+    decode at the same S against it too."""
+    p, ro, rl = _decode_problem("gqa", Lkv)
+    B, Hq, Hkv, Lq, Lkv, D = p.dims
+    if S == 0:
+        out, lse = _single_launch(skv, p, skv.pick_num_splits(B, Hkv, (Hq // Hkv) * Lq, Lkv, D))
+        _check_decode_rows(p, out, lse, ro, rl)
+        return
+    q, k, v = p.q.to(DEV), p.k.to(DEV), p.v.to(DEV)
+    op = torch.full((S,) + tuple(q.shape), float("nan"), dtype=torch.float32, device=DEV)
+    lp = torch.full((S, B, Hq, Lq), float("nan"), dtype=torch.float32, device=DEV)
+    skv.attn_splitkv_partial(q, k, v, num_splits=S, scale=p.scale, out_part=op, lse_part=lp)
+    mo = torch.full_like(q, float("nan"))
+    ml = torch.full((B, Hq, Lq), float("nan"), dtype=torch.float32, device=DEV)
+    skv.merge_state(op, lp, out=mo, lse=ml)
+    torch.cuda.synchronize()
+    po, pl = oracle.splitkv_partials(wl.bits(p.q), wl.bits(p.k), wl.bits(p.v), "bf16", S,
+                                     scale=p.scale)
+    assert_lse_close(lp.cpu(), pl, "partial lse")
+    assert_out_close(op.cpu(), po, "partial out")
+    _check_decode_rows(p, mo, ml, ro, rl)
+    out, lse = _single_launch(skv, p, S)
+    _check_decode_rows(p, out, lse, ro, rl)
 
 
 @pytest.mark.parametrize("Lkv,sign", [(16384, 1), (16384, -1), (32768, 1), (32768, -1)])
 def test_wide_decode_full_size(skv, Lkv, sign):
-    """B4 Hq16 Hkv4 Lq4 D256 decode, q = 8 N(0,1), K offset by +-2: score range of
-    hundreds of nats."""
-    p = wl.wide_decode(Lkv, sign)
-    _decode_full(skv, p, n_rows=32, seed=Lkv + sign)
+    """B4 Hq16 Hkv4 Lq4 D256 decode, q = 8 N(0,1), K offset by +-2 (score range of
+    hundreds of nats), the split count bench.py uses: all 256 rows."""
+    p, ro, rl = _decode_problem("wide", Lkv, sign)
+    B, Hq, Hkv, Lq, Lkv, D = p.dims
+    S = skv.pick_num_splits(B, Hkv, (Hq // Hkv) * Lq, Lkv, D)
+    out, lse = _single_launch(skv, p, S)
+    _check_decode_rows(p, out, lse, ro, rl)
 
 
 def test_varlen_causal_full_size(skv):
