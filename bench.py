@@ -73,6 +73,23 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# Phase markers for kernel traces: before each measured phase a float64 fill kernel
+# (bench.py launches no other float64 kernel) marks where the phase's launches begin
+# in a rocprofv3 kernel trace, and PHASES lists the phases in order, each with the
+# labels of its launchers: the k-th library launch of a phase belongs to launcher
+# k mod len(labels) (launchers there are single kernels, issued round-robin).  The
+# JSON line carries PHASES, so a trace of this run splits into one row per workload.
+PHASES = []
+_MARK = []
+
+
+def phase(name, labels=None):
+    if not _MARK:
+        _MARK.append(torch.empty(16, dtype=torch.float64, device="cuda"))
+    _MARK[0].fill_(float(len(PHASES)))
+    PHASES.append(dict(name=name, labels=list(labels or [name])))
+
+
 # ------------------------------------------------------------------ helpers
 
 class Decode:
@@ -122,6 +139,11 @@ class Decode:
         """Algorithmic bytes of the decode: K + V + Q read, out (16-bit) + LSE written."""
         B, Hq, Hkv, Lq, Lkv, D = self.dims
         return self.partial_bytes() + B * Hq * Lq * D * 2 + B * Hq * Lq * 4
+
+
+def _ws_dims(d, S):
+    B, Hq, Hkv, Lq, Lkv, D = d.dims
+    return B, Hq, Lq, D, S, Hkv
 
 
 def capture(fn):
@@ -233,6 +255,7 @@ def headline(skv, args):
         for d in dec:
             d.step()
 
+    phase("decode_gqa step (graph)", [f"decode_gqa Lkv{L}" for L in lkvs])
     g = capture(step)
     for _ in range(args.warmup):
         g.replay()
@@ -251,12 +274,16 @@ def headline(skv, args):
     # durations per launch from HIP events.  The two-kernel form (partials, then
     # merge_state) is timed too, for comparison.
     reps = max(5, args.steps)
+    phase("decode_gqa single launch", [f"decode_gqa Lkv{L} S{d.S}" for L, d in zip(lkvs, dec)])
     fused = [stats(x) for x in kernel_durations([d.step for d in dec], reps, per_rep=True)]
     fused_us = [st["mean"] for st in fused]
+    phase("decode_gqa step (graph, events)", [f"decode_gqa Lkv{L}" for L in lkvs])
     step_st = time_graph(g, reps)
     launchers = []
     for d in dec:
         launchers += [d.partial, d.merge]
+    phase("decode_gqa two-kernel", [f"decode_gqa Lkv{L} {w}" for L in lkvs
+                                      for w in ("partial", "merge")])
     durs = kernel_durations(launchers, reps)
     part_us = [durs[2 * i] for i in range(len(dec))]
     merge_us = [durs[2 * i + 1] for i in range(len(dec))]
@@ -264,17 +291,39 @@ def headline(skv, args):
     avg_bytes = sum(d.step_bytes() for d in dec) / len(dec)
     achieved = avg_bytes / (avg_us * 1e-6) / 1e9
 
+    # the single-launch decode at the chunk counts of config 2 (8 to 32) and at 4, the
+    # three problems interleaved as in the step (cold HBM); same buffers, own workspaces
+    sweep_S = (4, 8, 16, 32)
+    sweep = {}
+    for S in sweep_S:
+        wss = [torch.zeros(d.skv.splitkv_workspace_bytes(*_ws_dims(d, S)), dtype=torch.uint8,
+                           device="cuda") for d in dec]
+        fns = [(lambda d=d, w=w, S=S: d.skv.attn_splitkv_decode(
+            d.q, d.k, d.v, num_splits=S, scale=d.scale, out=d.out, lse=d.lse, workspace=w))
+            for d, w in zip(dec, wss)]
+        phase(f"decode_gqa single launch num_splits={S}",
+              [f"decode_gqa Lkv{L} S{S}" for L in lkvs])
+        sweep[S] = [stats(x) for x in kernel_durations(fns, reps, per_rep=True)]
+        del wss
+
     # per problem, from the same event passes (problems run in step order: cold HBM)
     per = {}
     for i, (L, d) in enumerate(zip(lkvs, dec)):
         us = fused_us[i]
         gbs = d.step_bytes() / (us * 1e-6) / 1e9
+        by_s = {}
+        for S in sweep_S:
+            u = sweep[S][i]["mean"]
+            by_s[str(S)] = dict(us=round(u, 2), frac=round(d.step_bytes() / (u * 1e-6) / 1e9 /
+                                                        HBM_PEAK_GBS, 4),
+                                p50_us=round(sweep[S][i]["p50"], 2))
         per[str(L)] = dict(num_splits=d.S, us=round(us, 2), gbs=round(gbs, 1),
                            frac=round(gbs / HBM_PEAK_GBS, 4),
                            p10_us=round(fused[i]["p10"], 2), p50_us=round(fused[i]["p50"], 2),
                            p90_us=round(fused[i]["p90"], 2),
                            two_kernel_us=round(part_us[i] + merge_us[i], 2),
-                           partial_us=round(part_us[i], 2), merge_us=round(merge_us[i], 2))
+                           partial_us=round(part_us[i], 2), merge_us=round(merge_us[i], 2),
+                           single_launch_by_num_splits=by_s)
     return dec, dict(ms=ms, value=value, step_bytes=step_bytes, achieved=achieved,
                      avg_us=avg_us, avg_bytes=avg_bytes, per=per, step_st=step_st)
 
@@ -345,11 +394,34 @@ def secondary(skv, args, dec):
     def partly_filled():
         skv.attn_splitkv_decode(d32.q, d32.k, d32.v, num_splits=d32.S, scale=d32.scale,
                                 out=d32.out, lse=d32.lse, workspace=d32.ws, kv_len=kvl)
-    st = stats(kernel_durations([partly_filled], reps, per_rep=True)[0])
+    # each timed launch follows a full decode of the 1.07 GB Lkv-32768 problem, which
+    # evicts the 256 MB Infinity Cache: the filled keys are read cold
+    phase("decode_gqa kv_len", ["capacity32768 kv_len4096", "evicting Lkv32768 decode"])
+    st = stats(kernel_durations([partly_filled, d32.step], reps, per_rep=True)[0])
     us = st["p50"]
     fb = 2 * B * Hkv * filled * D * 2 + 2 * B * Hq * Lq * D * 2 + B * Hq * Lq * 4
     res["decode_gqa_capacity32768_kvlen4096"] = dict(
-        **pct(st), gbs=round(fb / (us * 1e-6) / 1e9, 1), num_splits=d32.S, filled_bytes=fb)
+        **pct(st), gbs=round(fb / (us * 1e-6) / 1e9, 1), frac_hbm=round(fb / (us * 1e-6) / 1e9 /
+                                                                       HBM_PEAK_GBS, 4),
+        num_splits=d32.S, filled_bytes=fb, cache="cold (each launch follows a 1.07 GB decode)")
+
+    # small-query GQA decode with more query rows per kv head (G x Lq = 32 and 64):
+    # B8 Hkv8 D128 bf16 Lkv 8192, G = 8 and 16 with Lq = 4; the two problems alternate
+    # (268 MB of K/V each), so each reads what the other evicted
+    many = []
+    for G in (8, 16):
+        log(f"generating decode G={G} Lq=4")
+        many.append((G, Decode(skv, wl.decode_gqa(8192, seed=40 + G, Hq=8 * G, Lq=4))))
+    phase("decode many rows", [f"G{G} Lq4 rows{4 * G}" for G, _ in many])
+    durs = kernel_durations([d.step for _, d in many], reps, per_rep=True)
+    for i, (G, d) in enumerate(many):
+        st = stats(durs[i])
+        us = st["p50"]
+        gbs = d.step_bytes() / (us * 1e-6) / 1e9
+        res[f"decode_gqa_G{G}_Lq4_rows{4 * G}_B8_Hkv8_Lkv8192_D128"] = dict(
+            **pct(st), gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4), num_splits=d.S)
+    del many, durs
+    torch.cuda.empty_cache()
 
     # wide-head decode: B4 Hq16 Hkv4 Lq4 D256, K offset +2; the two problems
     # alternate, so each reads what the other evicted
@@ -358,6 +430,7 @@ def secondary(skv, args, dec):
         log(f"generating wide_decode Lkv={L}")
         wides.append((L, Decode(skv, wl.wide_decode(L, +1))))
     launchers = [d.step for _, d in wides]
+    phase("decode wide D256", [f"wide Lkv{L}" for L, _ in wides])
     durs = kernel_durations(launchers, reps, per_rep=True)
     for i, (L, d) in enumerate(wides):
         st = stats(durs[i])
@@ -379,6 +452,7 @@ def secondary(skv, args, dec):
 
     def varlen():
         skv.attn_fwd_varlen(q, k, v, cq, ck, mx, scale=vl.scale, causal=True, out=out, lse=lse)
+    phase("prefill varlen causal")
     st = time_graph(capture(varlen), reps)
     us = st["p50"]
     fl = wl.prefill_flops(vl.lengths, 32, 128, causal=True)
@@ -413,6 +487,7 @@ def secondary(skv, args, dec):
     fl = 4 * 16 * 8192 * 8192 * 64
     for name, fn in (("prefill_ring_4chunks_smooth_merge_H16_S8192_D64_fp16", ring),
                      ("prefill_full_H16_S8192_D64_fp16", full)):
+        phase(name)
         st = time_graph(capture(fn), reps)
         us = st["p50"]
         tf = fl / (us * 1e-6) / 1e12
@@ -436,6 +511,7 @@ def secondary(skv, args, dec):
         skv.sage_fwd(q, kf, vf, scale=rc["scale"], smooth_k=True, out=fo, lse=fl_, workspace=wsf)
     for name, fn in (("prefill_int8qk_ring_4chunks_smooth_merge_H16_S8192_D64_fp16", ring_int8),
                      ("prefill_int8qk_full_smooth_H16_S8192_D64_fp16", full_int8)):
+        phase(name)
         st = time_graph(capture(fn), reps)
         us = st["p50"]
         tf = fl / (us * 1e-6) / 1e12
@@ -460,11 +536,13 @@ def secondary(skv, args, dec):
     def dense8():
         skv.sage_fwd(q, k, v, scale=p.scale, smooth_k=True, out=out, lse=lse, workspace=wsd)
     fl = 4 * 32 * 8192 * 8192 * 128
+    phase("prefill_dense_H32_Hkv8_S8192_D128_bf16")
     st = time_graph(capture(dense16), reps)
     us = st["p50"]
     tf = fl / (us * 1e-6) / 1e12
     res["prefill_dense_H32_Hkv8_S8192_D128_bf16"] = dict(
         **pct(st), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4), flop=fl)
+    phase("prefill_int8qk_dense_smooth_H32_Hkv8_S8192_D128_bf16")
     st = time_graph(capture(dense8), reps)
     us = st["p50"]
     tf = fl / (us * 1e-6) / 1e12
@@ -482,6 +560,7 @@ def secondary(skv, args, dec):
 
     def tiny():
         skv.attn_fwd(tq, tk, tv, scale=d["scale"], out=to, lse=tl)
+    phase("tiny_lse_B1_H4_Sq64_Sk1000_D128")
     res["tiny_lse_B1_H4_Sq64_Sk1000_D128"] = pct(time_graph(capture(tiny), reps))
     return res
 
@@ -613,6 +692,7 @@ def main():
         "parity_sample_max_err": round(err, 5),
         "secondary": sec,
         "practical_ceilings": ceil,
+        "trace_phases": PHASES,
     }
     print(json.dumps(line), flush=True)
 

@@ -273,9 +273,9 @@ skv_status_t prepare_split(const void* q, const void* k, const void* v, int B, i
     if (st != SKV_OK) return st;
     if (!valid_layout(layout)) return fail(SKV_EINVAL, "unknown layout code %d", (int)layout);
     if (!std::isfinite(scale)) return fail(SKV_EINVAL, "scale must be finite");
-    if ((int64_t)(Hq / Hkv) * Lq > 16)
-        return fail(SKV_EUNSUPPORTED, "(Hq/Hkv)*Lq = %lld query rows per kv head exceeds 16",
-                    (long long)(Hq / Hkv) * Lq);
+    if ((int64_t)(Hq / Hkv) * Lq > skv::splitkv_max_rows(D))
+        return fail(SKV_EUNSUPPORTED, "(Hq/Hkv)*Lq = %lld query rows per kv head exceeds %d at D = %d",
+                    (long long)(Hq / Hkv) * Lq, skv::splitkv_max_rows(D), D);
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
         return fail(SKV_EINVAL, "q, k and v must be 16-byte aligned");
     if (kv_len && !aligned(kv_len, 4)) return fail(SKV_EINVAL, "kv_len must be 4-byte aligned");
@@ -294,6 +294,7 @@ skv_status_t prepare_split(const void* q, const void* k, const void* v, int B, i
     a.kv_head = hnd ? (int64_t)Lkv * D : D;
     a.kv_batch = (int64_t)Hkv * Lkv * D;
     a.part_stride = (int64_t)B * Hq * Lq * D;
+    a.group = 1;
     a.scale_log2 = scale * 1.4426950408889634f;
     return SKV_OK;
 }
@@ -373,6 +374,11 @@ skv_status_t launch_decode(skv::SplitArgs& a, int D, skv_dtype_t dtype, void* ws
     a.ticket = (int*)ws;
     a.out_part = (float*)(ws + skv::kTicketBlockBytes);
     a.lse_part = (float*)(ws + skv::kTicketBlockBytes + po_bytes);
+    // A work group takes `group` consecutive chunks, so that a launch keeps about the
+    // work-group count the split heuristic targets whatever num_splits is: its online
+    // softmax over those chunks' keys gives the merge of their partial states.
+    const int target = skv_pick_num_splits(a.B, a.Hkv, (a.Hq / a.Hkv) * a.Lq, a.Lkv, D);
+    a.group = a.num_splits / target > 1 ? a.num_splits / target : 1;
     return launched(skv::launch_splitkv(a, dtype, D, true, stream), "splitkv_decode");
 }
 

@@ -58,6 +58,9 @@ struct SplitArgs {
     int64_t q_row, q_head, q_batch;
     int64_t kv_row, kv_head, kv_batch;
     int64_t part_stride;        // elements between consecutive splits of out_part
+    // consecutive chunks one work group takes (1 for the partial states; the
+    // single-launch decode may group chunks, gridDim.x = ceil(num_splits / group))
+    int group;
     float scale_log2;
     // single-launch decode only: merged output (q's dtype and strides), its LSE
     // [B, Hq, Lq] (nullable) and one arrival ticket per (batch, kv head)
@@ -132,6 +135,7 @@ constexpr int kMaxDecodeSplits = 256;  // single-launch decode: its merge walks 
 constexpr int kMaxDecodeUnits = 65536;
 constexpr size_t kTicketBlockBytes = (size_t)kMaxDecodeUnits * sizeof(int);
 hipError_t launch_splitkv(const SplitArgs& a, int dtype, int D, bool fused, hipStream_t stream);
+int splitkv_max_rows(int D);   // query rows per kv head, (Hq / Hkv) * Lq, the decode serves
 // Device-resident scratch of the no-allocation decode (scratch.hip): counters then
 // partial states, 16 MiB per device.  noalloc_scratch() returns this device's address
 // of it (looked up once per device, counters zeroed on first use).

@@ -141,7 +141,8 @@ def test_splitkv_rejects(lib):
     assert call(Lq=0) == 1
     assert call(Lkv=-1) == 1
     assert call(Hq=30) == 1
-    assert call(Lq=5) == 2           # (32/8)*5 = 20 rows per kv head > 16
+    assert call(Lq=17) == 2          # (32/8)*17 = 68 rows per kv head > 64
+    assert call(Lq=5, D=256) == 2    # 20 rows > 16 at D = 256
     assert call(D=80) == 2
     assert call(kv_len=ctypes.c_void_p(0x10002)) == 1   # kv_len misaligned
     assert call(B=0) == 0

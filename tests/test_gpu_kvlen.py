@@ -78,6 +78,7 @@ SWEEP = [
     (3, 32, 8, 1, 4097, 128, 4),
     (2, 8, 1, 2, 12345, 128, 32),
     (2, 8, 2, 1, 40000, 128, 8),
+    (2, 32, 1, 2, 3001, 128, 24),     # 64 rows per kv head
 ]
 
 

@@ -174,6 +174,10 @@ SPLIT_CASES = [
     (2, 8, 2, 2, 1, 64, 4),           # one key: three empty chunks
     (1, 16, 1, 1, 4096, 128, 1),      # 16 rows per kv head, one chunk
     (1, 4, 2, 1, 0, 128, 3),          # no key at all
+    (2, 64, 8, 4, 1500, 128, 8),      # G = 8, Lq = 4: 32 rows per kv head
+    (1, 64, 4, 4, 999, 128, 5),       # G = 16, Lq = 4: 64 rows per kv head
+    (2, 32, 2, 3, 700, 64, 16),       # 48 rows per kv head at D = 64
+    (1, 16, 2, 3, 2049, 64, 3),       # 24 rows per kv head, ragged key tail
 ]
 
 
