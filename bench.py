@@ -567,12 +567,12 @@ def secondary(skv, args, dec):
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_gqa_splitkv_decode_hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "split_kv_merge_amd", "csrc", f)
-                  for f in ("splitkv.hip", "device.h", "launch.h")]
+                  for f in ("splitkv.hip", "splitkv_tail.h", "device.h", "launch.h")]
 
 
 def kernel_source_sha():
     """SHA-256 of the decode kernel's sources with comments and whitespace removed:
-    splitkv.hip, device.h and, of launch.h, only the decode's argument block
+    splitkv.hip, splitkv_tail.h, device.h and, of launch.h, only the decode's argument block
     (struct SplitArgs), so that the counter record goes stale when the decode's code
     changes, not its comments or other kernels' declarations."""
     import hashlib

@@ -20,8 +20,12 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libskv.so")
 INCLUDE = os.path.join(ROOT, "include")
 
-SOURCES = ["api.cpp", "fmha_fwd.hip", "splitkv.hip", "merge.hip", "kmean.hip",
-           "sage_quant.hip", "sage_fwd.hip", "scratch.hip"]
+SOURCES = ["api.cpp", "fmha_fwd.hip", "splitkv.hip", "splitkv_wide.hip", "merge.hip",
+           "kmean.hip", "sage_quant.hip", "sage_fwd.hip", "scratch.hip"]
+# Per-file flags: the many-row decode kernel keeps its output accumulators in AGPRs
+# through asm MFMAs and needs its builtin MFMAs in VGPR form, so that the scores stay
+# in VGPRs instead of moving between the register files.
+EXTRA_FLAGS = {"splitkv_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
@@ -39,7 +43,8 @@ def common_flags():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src),
+                                                                 "-o", obj]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

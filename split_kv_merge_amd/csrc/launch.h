@@ -135,6 +135,9 @@ constexpr int kMaxDecodeSplits = 256;  // single-launch decode: its merge walks 
 constexpr int kMaxDecodeUnits = 65536;
 constexpr size_t kTicketBlockBytes = (size_t)kMaxDecodeUnits * sizeof(int);
 hipError_t launch_splitkv(const SplitArgs& a, int dtype, int D, bool fused, hipStream_t stream);
+// 17..64 query rows per kv head at D = 64, 128 (splitkv_wide.hip); grid (parts, Hkv, B)
+hipError_t launch_splitkv_wide(const SplitArgs& a, int dtype, int D, bool fused, dim3 grid,
+                               hipStream_t stream);
 int splitkv_max_rows(int D);   // query rows per kv head, (Hq / Hkv) * Lq, the decode serves
 // Device-resident scratch of the no-allocation decode (scratch.hip): counters then
 // partial states, 16 MiB per device.  noalloc_scratch() returns this device's address
