@@ -31,7 +31,8 @@ the median (`us`) of 50 graph replays, each timed with its own HIP events, with
 p10 / p90 and the mean beside it.  `practical_ceilings` are the micro-benchmarks of
 microbench/ceilings.hip run in the same process (HBM read stream with plain and with
 nontemporal loads, bf16 MFMA, ...); every decode and prefill figure is also given
-as a fraction of them (`frac_practical`, `frac_mfma_practical`).
+as a fraction of them (`frac_practical`, `frac_mfma_practical`, and for prefill
+`frac_gemm_practical`: the rate over a bf16 8192^3 vendor-library GEMM's on the same GPU).
 """
 from __future__ import annotations
 
@@ -348,9 +349,53 @@ def parity_sample(dec):
     return max(errs)
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), else what platform reports."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+# The oracle's config-1 attention (B1 H4 Sq64 Sk1000 D128: the graded-row query, fp64),
+# timed in a child process started with OMP_NUM_THREADS=1 so that it runs on one core.
+_C1_SINGLE_CORE = r"""
+import json, sys, time
+sys.path.insert(0, sys.argv[1])
+import oracle, workloads as wl
+d = wl.tiny_lse()
+args = (wl.bits(d["q_graded"]), wl.bits(d["k"]), wl.bits(d["v"]), "bf16")
+oracle.attn(*args, scale=d["scale"])
+ts = []
+for _ in range(5):
+    t = time.perf_counter()
+    oracle.attn(*args, scale=d["scale"])
+    ts.append(time.perf_counter() - t)
+print(json.dumps(sorted(ts)[2]))
+"""
+
+
+def c1_single_core_ms():
+    """Milliseconds per call of the oracle's config-1 attention on one core (median of 5
+    calls), or None when the child process fails."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        r = subprocess.run([sys.executable, "-c", _C1_SINGLE_CORE, ROOT], env=env,
+                           capture_output=True, text=True, timeout=300)
+        return round(float(r.stdout.strip().splitlines()[-1]) * 1e3, 2)
+    except (subprocess.SubprocessError, ValueError, IndexError):
+        return None
+
+
 def cpu_baseline(dec, args):
     """The oracle's decode step (fp64 per-chunk partials + merge, same split counts) on
-    the same three problems, repeated until at least 10 s of host time has passed."""
+    the same three problems, repeated until at least 10 s of host time has passed; with
+    the host's CPU model, OMP_NUM_THREADS as set, and the config-1 oracle on one core."""
     import oracle
     import workloads as wl
     cores = len(os.sched_getaffinity(0))
@@ -370,7 +415,12 @@ def cpu_baseline(dec, args):
                 kind="oracle",
                 sample=f"the whole decode step (Lkv 4096, 8192, 32768; B=8 Hq=32 Hkv=8 D=128), "
                        f"fp64 partials + merge, {reps} repetition(s) in {sec:.1f} s",
-                cpu=platform.processor() or platform.machine())
+                cpu=cpu_model(), cpus_available=cores,
+                omp_num_threads=os.environ.get("OMP_NUM_THREADS"),
+                c1_single_core_ms=c1_single_core_ms(),
+                c1_single_core="the oracle's config-1 attention (B1 H4 Sq64 Sk1000 D128, fp64, "
+                               "graded-row query) on one core (OMP_NUM_THREADS=1), median of "
+                               "5 calls")
 
 
 def secondary(skv, args, dec):
@@ -643,6 +693,7 @@ def main():
         # the same figures against the practical ceilings measured above
         hbm = ceil["hbm_read_stream_nontemporal_GBs"]
         mfma = ceil["mfma_bf16_32x32x16_tflops"]
+        gemm = ceil.get("gemm_bf16_8192_tflops")
         for v in h["per"].values():
             v["frac_practical"] = round(v["gbs"] / hbm, 4)
         for v in sec.values():
@@ -650,6 +701,8 @@ def main():
                 v["frac_practical"] = round(v["gbs"] / hbm, 4)
             if "frac_mfma" in v:
                 v["frac_mfma_practical"] = round(v["tflops"] / mfma, 4)
+                if gemm:
+                    v["frac_gemm_practical"] = round(v["tflops"] / gemm, 4)
     line = {
         "metric": METRIC,
         "value": round(h["value"], 1),

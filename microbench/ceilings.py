@@ -64,6 +64,22 @@ def measure():
             sec = t(which, grid, 0, ctypes.c_void_p(buf.data_ptr()), buf.numel() // 16)
             best = max(best, buf.numel() / sec / 1e9)
         res[key] = best
+    del buf
+    # A vendor-library GEMM (torch.matmul, hipBLASLt on ROCm), bf16 8192^3: what a kernel
+    # that streams its MFMA operands through memory and LDS reaches on this machine, as
+    # opposed to the register-only MFMA loop above.
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    res["gemm_bf16_8192_tflops"] = 2 * 8192 ** 3 / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e12
     return res
 
 

@@ -40,3 +40,15 @@ def test_traffic_record_matches_the_current_decode_kernel():
                                  "retake FETCH_SIZE / WRITE_SIZE for the current decode kernel")
     # one decode launch of the benchmark reads at least its K/V and writes its output
     assert 0.95 * 492263765 <= traffic <= 1.10 * 492263765
+
+
+def test_cpu_baseline_names_the_host_cpu_model():
+    name = bench.cpu_model()
+    assert isinstance(name, str) and name.strip()
+    try:
+        models = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                  if l.startswith("model name")]
+    except OSError:
+        models = []
+    if models:
+        assert name == models[0]

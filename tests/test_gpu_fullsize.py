@@ -127,6 +127,32 @@ def test_wide_decode_full_size(skv, Lkv, sign):
     _check_decode_rows(p, out, lse, ro, rl)
 
 
+@pytest.mark.parametrize("G", [8, 16])
+def test_many_row_decode_full_size(skv, G):
+    """B8 Hkv8 Lkv8192 D128 decode with G query heads per kv head at Lq = 4 (32 and 64
+    rows per kv head), the problems of bench.py's many-row lines, at the split count it
+    uses: 160 sampled rows (plus the first and last of every batch element) against the
+    oracle, every row against the range property."""
+    p = wl.decode_gqa(8192, seed=40 + G, Hq=8 * G, Lq=4)
+    B, Hq, Hkv, Lq, Lkv, D = p.dims
+    S = skv.pick_num_splits(B, Hkv, G * Lq, Lkv, D)
+    out, lse = _single_launch(skv, p, S)
+    v = p.v.to(DEV)
+    vmin = v.float().amin(dim=2).repeat_interleave(G, dim=1)[:, :, None, :]
+    vmax = v.float().amax(dim=2).repeat_interleave(G, dim=1)[:, :, None, :]
+    torch.cuda.synchronize()
+    o = out.float()
+    assert torch.isfinite(lse).all() and torch.isfinite(o).all()
+    slack = 1e-2 + 1e-2 * torch.maximum(vmin.abs(), vmax.abs())
+    assert ((o >= vmin - slack) & (o <= vmax + slack)).all()
+    rows = _sample_rows(B, Hq, Lq, 160, seed=60 + G)
+    ro, rl = oracle.attn_rows(wl.bits(p.q), wl.bits(p.k), wl.bits(p.v), "bf16", rows,
+                              scale=p.scale)
+    o_c, l_c = o.cpu().numpy(), lse.cpu().numpy()
+    assert_lse_close(np.array([l_c[b, h, i] for b, h, i in rows]), rl, "lse")
+    assert_out_close(np.stack([o_c[b, h, i] for b, h, i in rows]), ro, "out")
+
+
 def test_varlen_causal_full_size(skv):
     """16 packed sequences, lengths U[128, 4096], Hq32 Hkv8 D128 bf16, causal."""
     vl = wl.varlen_prefill(seed=4)

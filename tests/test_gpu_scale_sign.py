@@ -109,3 +109,38 @@ def test_sage_fwd_all_zero_key_blocks_in_masked_tiles(skv):
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     assert_lse_close(lse.cpu(), rl)
     assert_out_close(out.cpu(), ro)
+
+
+DECODE_CASES = [
+    # B, Hq, Hkv, Lq, Lkv, D, S: 4, 32 and 64 query rows per kv head, and 24 at D = 64
+    (2, 8, 2, 1, 777, 128, 3),
+    (1, 32, 4, 4, 777, 128, 3),
+    (1, 64, 4, 4, 650, 128, 2),
+    (1, 16, 2, 3, 901, 64, 4),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES)
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_splitkv_decode_any_scale(skv, case, scale):
+    """Split partials + merge and the single-launch decode with a negative or zero logit
+    scale, ragged key tails included, against the oracle."""
+    B, Hq, Hkv, Lq, Lkv, D, S = case
+    p = wl.attn_problem(B, Hq, Hkv, Lq, Lkv, D, seed=321)
+    ro, rl = oracle.attn(wl.bits(p.q), wl.bits(p.k), wl.bits(p.v), "bf16", scale=scale)
+    q, k, v = p.q.to(DEV), p.k.to(DEV), p.v.to(DEV)
+    op = torch.full((S,) + tuple(q.shape), float("nan"), dtype=torch.float32, device=DEV)
+    lp = torch.full((S, B, Hq, Lq), float("nan"), dtype=torch.float32, device=DEV)
+    skv.attn_splitkv_partial(q, k, v, num_splits=S, scale=scale, out_part=op, lse_part=lp)
+    mo = torch.full_like(q, float("nan"))
+    ml = torch.full((B, Hq, Lq), float("nan"), dtype=torch.float32, device=DEV)
+    skv.merge_state(op, lp, out=mo, lse=ml)
+    ws = torch.zeros(skv.splitkv_workspace_bytes(B, Hq, Lq, D, S, Hkv), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, Hq, Lq), float("nan"), dtype=torch.float32, device=DEV)
+    skv.attn_splitkv_decode(q, k, v, num_splits=S, scale=scale, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    for name, o, l in (("partials + merge", mo, ml), ("single launch", out, lse)):
+        assert_lse_close(l.cpu(), rl, f"{name} lse")
+        assert_out_close(o.float().cpu(), ro, f"{name} out")
