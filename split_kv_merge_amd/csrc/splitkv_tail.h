@@ -58,8 +58,11 @@ __device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
 // is normalised by its own sum, so it lies in the range of V and the 16-bit type
 // holds it; the merge adds them in fp32), half the bytes the merging work group has
 // to pull in.  The merge keeps memory latency off serial chains: each thread owns Q
-// adjacent 4-column groups of one row and reads the partial LSEs and outputs of GS
-// parts per round trip (all issued together).  Across groups of GS it keeps a
+// 4-column groups of one row and reads the partial LSEs and outputs of GS parts per
+// round trip (all issued together).  The TPR threads of a row take its groups
+// round-robin (thread t: groups t, t + TPR, ...), so each load instruction reads
+// TPR * 8 contiguous bytes of every row it touches: whole cache lines, each requested
+// once, instead of a quarter of every line of the row.  Across groups of GS it keeps a
 // running max M of the part LSEs and rescales its sums by 2^(M_old - M_new) when M
 // grows; the result is the stable merge -- out = sum_s 2^(lse_s - M) o_s /
 // sum_s 2^(lse_s - M), lse = M + log2 of that sum -- with no exponent above 0.
@@ -107,10 +110,14 @@ __device__ __forceinline__ void merge_rows(const SplitArgs& a, int b, int hk, in
                                            int P) {
     using E = Elem<T>;
     constexpr int Q = NR * D / 64;     // 4-column groups per thread: 16 NR rows x D/4 / 256
+    constexpr int TPR = 16 / NR;       // threads per row
+    static_assert(TPR * Q * 4 == D, "the threads of a row cover its D columns");
     const int tid = threadIdx.x;
-    const int r = tid * Q / (D / 4);   // the row this thread merges
+    const int r = tid / TPR;           // the row this thread merges
     if (r >= R) return;
-    const int d0 = (tid * Q % (D / 4)) * 4;
+    const int t = tid % TPR;           // its groups: t + TPR q, columns 4 (t + TPR q) + [0, 4)
+    const int d0 = 4 * t;
+    constexpr int DQ = 4 * TPR;        // column step from one of its groups to the next
     // The partials are read with device-coherent (sc1) buffer loads, which miss any
     // stale line this XCD's L2 may hold, so no cache-wide invalidate is needed.
     // Byte offsets stay below 2^31 (checked on the host).
@@ -138,7 +145,7 @@ __device__ __forceinline__ void merge_rows(const SplitArgs& a, int b, int hk, in
 #pragma unroll
             for (int q = 0; q < Q; ++q)
                 x[u][q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                    po_rsrc, (int)((row_off + d0 + 4 * q + sp * a.part_stride) * 2), 0,
+                    po_rsrc, (int)((row_off + d0 + DQ * q + sp * a.part_stride) * 2), 0,
                     kCoherentLoad));
         }
         float mg = -INFINITY;
@@ -174,9 +181,9 @@ __device__ __forceinline__ void merge_rows(const SplitArgs& a, int b, int hk, in
         u32x2 packed;
         packed.x = E::pack2(acc[q][0] * inv, acc[q][1] * inv);
         packed.y = E::pack2(acc[q][2] * inv, acc[q][3] * inv);
-        *reinterpret_cast<u32x2*>((uint16_t*)a.out + row_off + d0 + 4 * q) = packed;
+        *reinterpret_cast<u32x2*>((uint16_t*)a.out + row_off + d0 + DQ * q) = packed;
     }
-    if (d0 == 0 && a.lse) a.lse[lse_row] = W > 0.f ? M + fast_log2(W) : -INFINITY;
+    if (t == 0 && a.lse) a.lse[lse_row] = W > 0.f ? M + fast_log2(W) : -INFINITY;
 }
 
 }  // namespace dec

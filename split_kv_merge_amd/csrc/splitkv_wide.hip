@@ -98,18 +98,6 @@ __device__ __forceinline__ void o_fence(f32x16 (&o)[2][4]) {
                    "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
 }
 
-// max and sum of x over the lane pair (l, l ^ 32), in VALU (v_permlane32_swap)
-__device__ __forceinline__ float pair_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                    false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                    false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 template <typename T, int D, int NB, bool FUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void splitkv_wide_kernel(SplitArgs a) {
@@ -152,13 +140,13 @@ void splitkv_wide_kernel(SplitArgs a) {
     u32x4 qraw[QPT];
 #pragma unroll
     for (int u = 0; u < QPT; ++u) {
-        const int it = tid + 256 * u, r = it / CPR, cc = it % CPR;
-        qraw[u] = u32x4{0u, 0u, 0u, 0u};
-        if (r < R) {
-            const int hq = hk * G + r / a.Lq, iq = r % a.Lq;
-            qraw[u] = load16((const uint16_t*)a.q + (int64_t)b * a.q_batch +
-                             (int64_t)hq * a.q_head + (int64_t)iq * a.q_row + cc * 8) ^ qsign;
-        }
+        // rows past R load row R - 1 and are zeroed after the load, so the loads carry
+        // no branch and go out together
+        const int it = tid + 256 * u, r = it / CPR, cc = it % CPR, rc = min(r, R - 1);
+        const int hq = hk * G + rc / a.Lq, iq = rc % a.Lq;
+        const u32x4 raw = load16((const uint16_t*)a.q + (int64_t)b * a.q_batch +
+                                 (int64_t)hq * a.q_head + (int64_t)iq * a.q_row + cc * 8);
+        qraw[u] = r < R ? (raw ^ qsign) : u32x4{0u, 0u, 0u, 0u};
     }
 
     const uint16_t* kp = (const uint16_t*)a.k + (int64_t)b * a.kv_batch + (int64_t)hk * a.kv_head;
@@ -179,10 +167,15 @@ void splitkv_wide_kernel(SplitArgs a) {
     }
     typedef u32x4 KBuf[VCH];
     typedef u32x4 VBuf[VCH];
+    // The block's first key and key count are the same in every lane of the wave; read
+    // into scalar registers, they make the descriptors scalar, so each load is one
+    // instruction rather than a loop over the distinct descriptors of the lanes.
     auto load_block = [&](KBuf& kb_, VBuf& vb_, int blk, bool idle) {
-        const int kb = idle ? j0 : j0 + blk * kWideKeys;
-        const int nk = idle ? 1 : min(kWideKeys, j1 - kb);
-        const uint32_t nrec = (uint32_t)((nk - 1) * a.kv_row * 2 + D * 2);
+        const int kb = __builtin_amdgcn_readfirstlane(idle ? j0 : j0 + blk * kWideKeys);
+        const int nk = __builtin_amdgcn_readfirstlane(idle ? 1 : min(kWideKeys, j1 - kb));
+        // a chunk with no key reads nothing: num_records 0 makes every lane read zero
+        // without a memory access
+        const uint32_t nrec = nblk == 0 ? 0u : (uint32_t)((nk - 1) * a.kv_row * 2 + D * 2);
         const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(kp + (int64_t)kb * a.kv_row), (short)0, (int)nrec, kBufferRsrcWord3);
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
@@ -322,11 +315,12 @@ void splitkv_wide_kernel(SplitArgs a) {
     constexpr int W = kWideWaves;
     KBuf k0, k1, k2, k3;
     VBuf v0, v1, v2, v3;
-    if (wave < nblk) {
-        load_block(k0, v0, wave, false);
-        load_block(k1, v1, wave + W, wave + W >= nblk);
-        if constexpr (NB == 1) load_block(k2, v2, wave + 2 * W, wave + 2 * W >= nblk);
-    }
+    // Issued on every path (idle loads for a wave with no block), so the compiler's
+    // count of loads in flight is the same on all of them and the wait for Q below
+    // leaves the K/V requests in flight.
+    load_block(k0, v0, wave, wave >= nblk);
+    load_block(k1, v1, wave + W, wave + W >= nblk);
+    if constexpr (NB == 1) load_block(k2, v2, wave + 2 * W, wave + 2 * W >= nblk);
     // Q rows to LDS (the compiler waits for the Q loads only), then a barrier that
     // waits for LDS writes alone: __syncthreads would also wait for the K/V requests.
 #pragma unroll
