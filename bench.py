@@ -653,13 +653,13 @@ def measured_traffic():
 
 def practical_ceilings():
     """The practical ceilings of microbench/ceilings.hip, measured in this run (HBM read
-    stream with plain and with nontemporal loads, bf16 MFMA, LDS, exp/FMA rates), or
-    None when that library is not built."""
+    stream with plain and with nontemporal loads, bf16 MFMA, LDS, exp/FMA rates alone and
+    interleaved), or None when that library is not built."""
     if not os.path.exists(os.path.join(ROOT, "microbench", "libceilings.so")):
         return None
     sys.path.insert(0, os.path.join(ROOT, "microbench"))
     import ceilings
-    return {k: round(v, 1) for k, v in ceilings.measure().items()}
+    return {k: round(v, 3) if abs(v) < 10 else round(v, 1) for k, v in ceilings.measure().items()}
 
 
 def copy_probe():

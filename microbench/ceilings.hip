@@ -1,7 +1,8 @@
 // ceilings.hip -- micro-benchmarks for the practical ceilings the attention kernels
 // are measured against on MI355X (gfx950): LDS read bandwidth (16-byte reads and
 // the 64-bit transpose read), bf16 MFMA throughput, v_exp_f32 and v_fma_f32 issue
-// rates, and an HBM read stream (plain and nontemporal loads).  Measurement infrastructure only; nothing
+// rates, alone and interleaved (whether exponentials and FMAs share one pipe), and an
+// HBM read stream (plain and nontemporal loads).  Measurement infrastructure only; nothing
 // in the attention library uses it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -83,6 +84,37 @@ __global__ __launch_bounds__(256) void fma_f32(float* out, int iters) {
   float r = x0 + x1 + x2 + x3 + x4 + x5 + x6 + x7;
   if (r == 1234.5f) out[blockIdx.x] = r;
 }
+// v_exp_f32 alone (the -|x| folds into the source modifiers: one instruction per
+// element), then with one and with three independent FMAs per exponential.
+__global__ __launch_bounds__(256) void exp_only(float* out, int iters) {
+  float x0 = threadIdx.x * 1e-3f, x1 = x0 + 0.1f, x2 = x0 + 0.2f, x3 = x0 + 0.3f, x4 = x0+0.4f, x5=x0+0.5f, x6=x0+0.6f, x7=x0+0.7f;
+  for (int it = 0; it < iters; ++it) {
+    x0 = __builtin_amdgcn_exp2f(-__builtin_fabsf(x0)); x1 = __builtin_amdgcn_exp2f(-__builtin_fabsf(x1));
+    x2 = __builtin_amdgcn_exp2f(-__builtin_fabsf(x2)); x3 = __builtin_amdgcn_exp2f(-__builtin_fabsf(x3));
+    x4 = __builtin_amdgcn_exp2f(-__builtin_fabsf(x4)); x5 = __builtin_amdgcn_exp2f(-__builtin_fabsf(x5));
+    x6 = __builtin_amdgcn_exp2f(-__builtin_fabsf(x6)); x7 = __builtin_amdgcn_exp2f(-__builtin_fabsf(x7));
+  }
+  float r = x0 + x1 + x2 + x3 + x4 + x5 + x6 + x7;
+  if (r == 1234.5f) out[blockIdx.x] = r;
+}
+template <int NF>
+__global__ __launch_bounds__(256) void exp_fma(float* out, int iters) {
+  float x[8], y[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { x[j] = threadIdx.x * 1e-3f + 0.1f * j; y[j] = x[j] + 1.f; }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[j] = __builtin_amdgcn_exp2f(-__builtin_fabsf(x[j]));
+#pragma unroll
+      for (int f = 0; f < NF; ++f) y[j] = fmaf(y[j], 0.999f - 0.001f * f, 0.001f);
+    }
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r += x[j] + y[j];
+  if (r == 1234.5f) out[blockIdx.x] = r;
+}
 // HBM read stream: each work group streams its own contiguous range with eight
 // 16-byte loads in flight per thread, as plain loads or with the nontemporal hint.
 template <bool NT>
@@ -111,6 +143,9 @@ extern "C" int run(int which, void* p, int64_t n, void* out, int grid, int iters
     case 4: hipLaunchKernelGGL(fma_f32, dim3(grid), dim3(256), 0, s, (float*)out, iters); break;
     case 5: hipLaunchKernelGGL(hbm_read<false>, dim3(grid), dim3(256), 0, s, (const u32x4*)p, n, (uint32_t*)out); break;
     case 6: hipLaunchKernelGGL(hbm_read<true>, dim3(grid), dim3(256), 0, s, (const u32x4*)p, n, (uint32_t*)out); break;
+    case 7: hipLaunchKernelGGL(exp_only, dim3(grid), dim3(256), 0, s, (float*)out, iters); break;
+    case 8: hipLaunchKernelGGL(exp_fma<1>, dim3(grid), dim3(256), 0, s, (float*)out, iters); break;
+    case 9: hipLaunchKernelGGL(exp_fma<3>, dim3(grid), dim3(256), 0, s, (float*)out, iters); break;
   }
   return (int)hipGetLastError();
 }

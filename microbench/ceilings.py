@@ -57,6 +57,16 @@ def measure():
     res["exp_f32_lanes_per_clk_per_cu"] = g2 * 256 * 8 * 2000 / sec / CU / CLK
     sec = t(4, g2, 2000)
     res["fma_f32_lanes_per_clk_per_cu"] = g2 * 256 * 8 * 2000 / sec / CU / CLK
+    # Two waves per SIMD (the prefill kernels' occupancy): exponentials alone, then with
+    # one and three independent FMAs each.  A time ratio near 1 + (FMA time / exp time)
+    # means one shared pipe; near max(1, FMA time / exp time), separate pipes.
+    g3 = CU * 2
+    t_exp = t(7, g3, 4000)
+    t_fma = t(4, g3, 4000)
+    res["exp_only_f32_lanes_per_clk_per_cu"] = g3 * 256 * 8 * 4000 / t_exp / CU / CLK
+    res["fma_over_exp_time_2waves"] = t_fma / t_exp
+    res["exp_plus_fma_over_exp_time_2waves"] = t(8, g3, 4000) / t_exp
+    res["exp_plus_3fma_over_exp_time_2waves"] = t(9, g3, 4000) / t_exp
     buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
     for which, key in ((5, "hbm_read_stream_GBs"), (6, "hbm_read_stream_nontemporal_GBs")):
         best = 0.0
@@ -87,4 +97,4 @@ if __name__ == "__main__":
     if not os.path.exists(LIB):
         sys.exit("microbench/libceilings.so is not built")
     for k, v in measure().items():
-        print(f"{k}: {v:.1f}", flush=True)
+        print(f"{k}: {v:.3g}", flush=True)
