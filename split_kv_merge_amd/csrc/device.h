@@ -21,6 +21,10 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Buffer resource word 3 for raw (untyped) buffer access on gfx950.  A buffer load
+// past the descriptor's num_records returns zero without a memory access.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 // ---------------------------------------------------------------- 16-bit types
 
 template <typename T> struct Elem;

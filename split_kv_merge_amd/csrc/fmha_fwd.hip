@@ -136,6 +136,21 @@ void fmha_fwd_kernel(FmhaArgs a) {
     const int lrow = lane / CPR, lcol = (lane % CPR) * 8;
     uint16_t* qs = qo_lds[wave];
     uint16_t* const qsl = qs + lrow * QLD + lcol;  // chunk c of this lane: qsl + c * RPC * QLD
+    // mean(k) of this (batch | sequence, kv head) for the smoothing bias, this lane's
+    // half of D, requested together with Q so the prologue waits for one memory round
+    // trip.  Without smoothing the descriptor has length 0: the loads return zeros
+    // without a memory access, and the bias below is 0.
+    f32x4 kbv[NKK * 2];
+    {
+        const bool sm = a.kbar != nullptr;
+        const __amdgpu_buffer_rsrc_t kbr = __builtin_amdgcn_make_buffer_rsrc(
+            sm ? (void*)(a.kbar + ((int64_t)b * a.Hkv + g) * D) : (void*)a.q, (short)0,
+            sm ? D * 4 : 0, kBufferRsrcWord3);
+#pragma unroll
+        for (int i = 0; i < NKK * 2; ++i)
+            kbv[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   kbr, (hg * (D / 2) + 4 * i) * 4, 0, 0));
+    }
     // Q rows past the end read the last row: finite data whose results are never stored.
     u32x4 qraw[QCH];
 #pragma unroll
@@ -215,18 +230,19 @@ void fmha_fwd_kernel(FmhaArgs a) {
     for (int kk = 0; kk < NKK; ++kk)
         qf[kk] = as_vec8<T>(load16(&qs[n * QLD + hg * (D / 2) + kk * 8]) ^ qsign);
 
-    // Smoothing bias in log2 units: scale*log2(e) * (q_row . mean(k)).
-    float bias = 0.f;
-    if (a.kbar) {
-        const float* kb = a.kbar + ((int64_t)b * a.Hkv + g) * D + hg * (D / 2);
+    // Smoothing bias in log2 units: scale*log2(e) * (q_row . mean(k)) (0 without
+    // smoothing: the mean reads as zeros).
+    float bias;
+    {
         float acc = 0.f;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             u32x4 raw = __builtin_bit_cast(u32x4, qf[kk]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                acc += E::to_float((uint16_t)(raw[j] & 0xffff)) * kb[kk * 8 + 2 * j];
-                acc += E::to_float((uint16_t)(raw[j] >> 16)) * kb[kk * 8 + 2 * j + 1];
+                const int e = kk * 8 + 2 * j;   // element of this lane's half of D
+                acc += E::to_float((uint16_t)(raw[j] & 0xffff)) * kbv[e / 4][e % 4];
+                acc += E::to_float((uint16_t)(raw[j] >> 16)) * kbv[(e + 1) / 4][(e + 1) % 4];
             }
         }
         acc += xor_shfl(acc, 32);

@@ -9,9 +9,7 @@
 namespace skv {
 namespace dec {
 
-// Buffer resource word 3 for raw (untyped) buffer access on gfx950, and the
-// cache-policy bits of a buffer load: device-coherent (sc1), nontemporal (nt).
-constexpr int kBufferRsrcWord3 = 0x00020000;
+// Cache-policy bits of a buffer load: device-coherent (sc1), nontemporal (nt).
 constexpr int kCoherentLoad = 0x10;
 constexpr int kNontemporalLoad = 0x2;   // nt: a streaming read
 
