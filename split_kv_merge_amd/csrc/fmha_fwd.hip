@@ -257,7 +257,11 @@ void fmha_fwd_kernel(FmhaArgs a) {
     // tiles skip rescaling O and l.  Every p = 2^(s - m_ref) stays <= 2^kTau.
     constexpr float kTau = 8.f;
     float m_ref = -INFINITY, l_run = 0.f;
-    const float c = a.scale_log2;
+    // Logit scale, at least the smallest normal float: with scale 0 (or a denormal one)
+    // s * c then shifts no logit by a representable amount (|s| * 2^-126 is far below
+    // half an ulp of any logit that is not itself below 2^-100, whose 2^x rounds to 1
+    // either way), and -inf * c is -inf, never NaN.
+    const float c = fmaxf(a.scale_log2, 1.17549435e-38f);
 
     // Lane roles for the transpose read of V^T operands.
     const int g16 = lane >> 4, e4 = (lane & 15) >> 2, q4 = lane & 3;
@@ -309,7 +313,22 @@ void fmha_fwd_kernel(FmhaArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one QK MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDB * NJB * 2 / (NJB * NKK), 0);
             }
-            if constexpr (MASK) {
+            if constexpr (MASK && D <= 128) {
+                // lane holds keys t*BN + 4hg + off, off = 32jb + 8(i/4) + i%4, of the
+                // tile; the visible ones are those up to the row's last key (the key
+                // tail and, causal, the diagonal), i.e. off <= lim: one compare with a
+                // constant per logit
+                int last = Lk - 1;
+                if (CAUSAL) last = min(last, row + diag);
+                const int lim = last - (t * BN + hg * 4);
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        s[jb][i] = jb * 32 + 8 * (i >> 2) + (i & 3) <= lim ? s[jb][i] : -INFINITY;
+            }
+            if constexpr (MASK && D > 128) {
+                // (per-key indexes: the bound form above makes this instantiation spill)
                 // lane holds keys 8(i/4) + 4hg + i%4 of each 32-key block
                 const int kbase = t * BN;
 #pragma unroll
@@ -342,12 +361,9 @@ void fmha_fwd_kernel(FmhaArgs a) {
             // p = 2^(s*c - bias - m_ref), packed to 16-bit as the B operand of PV.  The
             // row sum adds the packed (rounded) pairs with one dot2 against (1, 1): the
             // normaliser then sums exactly the P values the PV product uses.  Four
-            // partial sums keep the dependent chains short.  In masked tiles a masked
-            // logit gives p = 0 also when c = 0 (scale 0: every visible logit is 0).
-            auto logit = [&](float x) {
-                const float y = fmaf(x, c, nb);
-                return (MASK && x == -INFINITY) ? -INFINITY : y;
-            };
+            // partial sums keep the dependent chains short.  c > 0, so a masked logit
+            // (-inf) stays -inf and gives p = 0.
+            auto logit = [&](float x) { return fmaf(x, c, nb); };
             uint32_t pk[NJB][2][4];
             float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
