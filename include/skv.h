@@ -139,8 +139,10 @@ skv_status_t skv_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
  * chunks that hold no key, which get (0, -inf) [ET reviewer item 3: no early exit
  * for empty splits], so neither buffer needs initialising.  Merge the states with
  * skv_merge_state.
- * Limits: Lq >= 1, Lkv >= 0, num_splits >= 1, (Hq / Hkv) * Lq <= 16
- * (SKV_EUNSUPPORTED beyond).
+ * Limits: Lq >= 1, Lkv >= 0, num_splits >= 1; query rows per kv head
+ * (Hq / Hkv) * Lq <= 64 at D <= 128 and <= 16 at D = 256 (SKV_EUNSUPPORTED beyond).
+ * Every K/V byte of a chunk is read once for all of that kv head's query rows [ET
+ * reviewer item 1: the small-query range, Lq 2 to 4 with grouped heads].
  */
 skv_status_t skv_attn_splitkv_partial(const void* q, const void* k, const void* v,
                                       float* out_part, float* lse_part, int B, int Hq,
