@@ -170,6 +170,7 @@ void fmha_fwd_kernel(FmhaArgs a) {
     // the wave's last row, or any tile of a wave whose rows all lie past Lq, would
     // only add masked (-inf) logits -- exactly nothing -- so the wave skips its math
     // there (it still stages tiles and joins every barrier).
+    const bool wave_live = wrow0 < Lq;
     int wave_tiles = ntiles;
     if (wrow0 >= Lq)
         wave_tiles = 0;
@@ -272,8 +273,10 @@ void fmha_fwd_kernel(FmhaArgs a) {
     auto process = [&](int t, auto mask_c) {
         constexpr bool MASK = decltype(mask_c)::value;
         const int buf = t & 1;
-        // (unmasked tiles are computed by every wave: no branch in the hot loop)
-        if (!MASK || t < wave_tiles) {
+        // (a wave whose rows all lie past the sequence end skips unmasked tiles too:
+        // their results are never stored; the branch is uniform per wave.  Not at
+        // D = 256, where the branch makes the instantiation spill.)
+        if (MASK ? t < wave_tiles : (D > 128 || wave_live)) {
             // Operands from LDS, issued ahead of their MFMAs: the 16-byte K rows of
             // every k-step first, then the V^T transpose reads interleaved with the QK
             // MFMAs, so their latency hides behind the QK product and the softmax.
