@@ -79,6 +79,8 @@ SWEEP = [
     (2, 8, 1, 2, 12345, 128, 32),
     (2, 8, 2, 1, 40000, 128, 8),
     (2, 32, 1, 2, 3001, 128, 24),     # 64 rows per kv head
+    (3, 16, 1, 2, 777, 64, 8),        # 32 rows per kv head (one 32-row block), lengths 777, 1, 0
+    (2, 24, 1, 1, 100, 128, 16),      # 24 rows, 7-key chunks and empty ones
 ]
 
 
