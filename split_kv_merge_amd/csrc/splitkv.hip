@@ -35,11 +35,17 @@ constexpr float kTau = 8.f;   // lazy-rescale threshold of the running max (log2
 // (K and V) would not fit in the register file beside the rest of the wave's state.
 template <int D> constexpr int keys_per_block() { return D == 256 ? 16 : 32; }
 
+// K is staged through LDS at D = 256 only (see the kernel).
+template <int D> constexpr bool stage_k() { return D == 256; }
+
 template <int D> struct SplitLds {
     static constexpr int VLD = D + 16;  // V pitch (elements) in the staging slice
+    static constexpr int KLD = D + 8;   // K pitch (elements) in the staging slice
     static constexpr int OLD = D + 4;   // pitch (floats) of the combine buffer
     static constexpr int ROWS = 16;
-    static constexpr int STAGE = kWaves * keys_per_block<D>() * VLD * 2;
+    static constexpr int KOFF = kWaves * keys_per_block<D>() * VLD * 2;   // K slices (bytes)
+    static constexpr int STAGE =
+        KOFF + (stage_k<D>() ? kWaves * keys_per_block<D>() * KLD * 2 : 0);
     static constexpr int COMB = kWaves * (ROWS * OLD + 2 * ROWS) * 4;
     static constexpr int BYTES = STAGE > COMB ? STAGE : COMB;
 };
@@ -60,7 +66,9 @@ void splitkv_kernel(SplitArgs a) {
     constexpr int KPB = keys_per_block<D>();      // keys per block
     constexpr int NHF = KPB / 16;                 // 16-key halves per block
     constexpr int VCH = KPB * CPR / 64;           // V chunks per lane per block
-    constexpr int VLD = L::VLD, OLD = L::OLD, ROWS = L::ROWS;
+    constexpr int VLD = L::VLD, KLD = L::KLD, OLD = L::OLD, ROWS = L::ROWS;
+    constexpr bool KST = stage_k<D>();
+    static_assert(NHF * NKK == VCH, "K and V buffers hold the same number of chunks");
     static_assert(ROWS == 16, "one 16-row block on the MFMA N axis");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
@@ -109,21 +117,25 @@ void splitkv_kernel(SplitArgs a) {
     // masked out of the softmax, so no load needs a branch.  A prefetch past the
     // wave's last block (`idle`) reads only the range's first key row: the same
     // instructions, so the wait counts stay the same, but no second pass over a block.
-    typedef u32x4 KBuf[NHF][NKK];
+    typedef u32x4 KBuf[VCH];
     typedef u32x4 VBuf[VCH];
     auto load_block = [&](KBuf& kb_, VBuf& vb_, int blk, bool idle) {
         const int kb = j0 + blk * KPB;
+        if constexpr (!KST) {
+            // K in the operand layout: chunk hf*NKK + kk is k-step kk of keys 16hf + n
 #pragma unroll
-        for (int hf = 0; hf < NHF; ++hf) {
-            const int j = idle ? j0 : min(kb + hf * 16 + n, j1 - 1);
-            const uint16_t* kr = kp + (int64_t)j * a.kv_row + g4 * 8;
+            for (int hf = 0; hf < NHF; ++hf) {
+                const int j = idle ? j0 : min(kb + hf * 16 + n, j1 - 1);
+                const uint16_t* kr = kp + (int64_t)j * a.kv_row + g4 * 8;
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) kb_[hf][kk] = load16_stream(kr + kk * 32);
+                for (int kk = 0; kk < NKK; ++kk) kb_[hf * NKK + kk] = load16_stream(kr + kk * 32);
+            }
         }
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = lane + 64 * u;
             const int j = idle ? j0 : min(kb + c / CPR, j1 - 1);
+            if constexpr (KST) kb_[u] = load16_stream(kp + (int64_t)j * a.kv_row + (c % CPR) * 8);
             vb_[u] = load16_stream(vp + (int64_t)j * a.kv_row + (c % CPR) * 8);
         }
     };
@@ -134,6 +146,7 @@ void splitkv_kernel(SplitArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
 
     uint16_t* vl = (uint16_t*)smem + wave * KPB * VLD;
+    uint16_t* kl = (uint16_t*)(smem + L::KOFF) + wave * KPB * KLD;  // used when KST
     const int e4 = (lane & 15) >> 2, q4 = lane & 3;
 
     auto compute_block = [&](const KBuf& kc, const VBuf& vc, int blk) {
@@ -145,6 +158,7 @@ void splitkv_kernel(SplitArgs a) {
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = lane + 64 * u;
+            if constexpr (KST) store16(kl + (c / CPR) * KLD + (c % CPR) * 8, kc[u]);
             store16(vl + (c / CPR) * VLD + (c % CPR) * 8, vc[u]);
         }
         lds_wave_sync();
@@ -154,8 +168,11 @@ void splitkv_kernel(SplitArgs a) {
         for (int hf = 0; hf < NHF; ++hf) {
             sv[hf] = f32x4{};
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                sv[hf] = E::mfma16(as_vec8<T>(kc[hf][kk]), qf[kk], sv[hf]);
+            for (int kk = 0; kk < NKK; ++kk) {
+                const u32x4 kop = KST ? load16(kl + (hf * 16 + n) * KLD + kk * 32 + g4 * 8)
+                                      : kc[hf * NKK + kk];
+                sv[hf] = E::mfma16(as_vec8<T>(kop), qf[kk], sv[hf]);
+            }
         }
         float mx = -INFINITY;
 #pragma unroll
