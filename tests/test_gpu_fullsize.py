@@ -213,3 +213,28 @@ def test_ring_chunks_full_size(skv):
         assert np.isfinite(o).all() and np.isfinite(l).all(), name
         assert_lse_close(np.array([l[b, h, i] for b, h, i in rows]), rl, f"{name} lse")
         assert_out_close(np.stack([o[b, h, i] for b, h, i in rows]), ro, f"{name} out")
+
+
+@pytest.mark.parametrize("Sq,causal", [(8192, False), (8192, True), (1024, True)])
+def test_dense_d128_full_size(skv, Sq, causal):
+    """B1 Hq32 Hkv8 D128 bf16 against 8192 keys: the dense prefill bench problem
+    (Sq 8192, non-causal), the same causal, and a causal chunk of 1024 new rows after
+    7168 cached keys (row i sees keys up to i + 7168).  Sampled rows against the oracle,
+    including the rows on both sides of 256-row tile and 32-row wave-block boundaries,
+    and every output finite."""
+    p = wl.attn_problem(1, 32, 8, Sq, 8192, 128, seed=7 + (Sq != 8192))
+    q, k, v = p.q.to(DEV), p.k.to(DEV), p.v.to(DEV)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((1, 32, Sq), float("nan"), dtype=torch.float32, device=DEV)
+    skv.attn_fwd(q, k, v, scale=p.scale, causal=causal, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_c, l_c = out.float().cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(o_c).all() and np.isfinite(l_c).all()
+    rows = set(map(tuple, _sample_rows(1, 32, Sq, 32, seed=70 + causal + Sq).tolist()))
+    rows |= {(0, h, i % Sq) for h, i in ((3, 4095), (3, 4096), (17, 4127), (17, 4128),
+                                          (31, 255), (31, 256), (8, 1), (8, 8190))}
+    rows = np.array(sorted(rows), np.int64)
+    ro, rl = oracle.attn_rows(wl.bits(p.q), wl.bits(p.k), wl.bits(p.v), "bf16", rows,
+                              scale=p.scale, causal=causal)
+    assert_lse_close(np.array([l_c[b, h, i] for b, h, i in rows]), rl, "lse")
+    assert_out_close(np.stack([o_c[b, h, i] for b, h, i in rows]), ro, "out")
