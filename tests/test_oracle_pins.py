@@ -402,3 +402,63 @@ def test_gamma_bound_reproduces_printed_value_and_bounds_the_oracle():
     g = json.load(open(os.path.join(GOLDEN, "p5_gamma.json")))
     assert round(_gamma(g["n"], 2.0 ** -24), 7) == pytest.approx(g["gamma_n"], abs=5e-8)
     assert _gamma(256, 2.0 ** -53) < 3e-14
+
+
+# ------------------------------------------------------- structural identities
+
+def _small_problem(seed, Sq=5, Sk=37, D=16, Hq=2, Hkv=1):
+    p = wl.attn_problem(1, Hq, Hkv, Sq, Sk, D, seed=seed)
+    return p, wl.bits(p.q), wl.bits(p.k), wl.bits(p.v)
+
+
+def test_joint_key_value_permutation_changes_nothing():
+    """Non-causal attention is a sum over keys: permuting the K and V rows together
+    leaves out and LSE unchanged (to rounding order), while permuting V alone changes
+    out -- so a K/V index mismatch fails here."""
+    p, q, k, v = _small_problem(11)
+    perm = np.random.default_rng(3).permutation(k.shape[2])
+    o0, l0 = oracle.attn(q, k, v, "bf16", scale=p.scale)
+    o1, l1 = oracle.attn(q, k[:, :, perm], v[:, :, perm], "bf16", scale=p.scale)
+    assert np.abs(o1 - o0).max() < 1e-12 and np.abs(l1 - l0).max() < 1e-12
+    o2, _ = oracle.attn(q, k, v[:, :, perm], "bf16", scale=p.scale)
+    assert np.abs(o2 - o0).max() > 1e-3
+
+
+def test_value_shift_shifts_the_output():
+    """The softmax weights of a row sum to one, so adding a constant c to every V
+    element adds c to every output element and leaves the LSE alone.  V is drawn on
+    multiples of 1/64 in (-1, 1) and c = 1, so v and v + 1 are both exact in bf16."""
+    p, q, k, v = _small_problem(12)
+    rng = np.random.default_rng(12)
+    v_c = rng.integers(-63, 64, size=v.shape) / 64.0
+    v_base = _bf16(v_c)
+    v_shift = _bf16(v_c + 1.0)
+    assert np.array_equal(_dec(torch.from_numpy(v_shift.astype(np.int16)).view(torch.bfloat16)),
+                          v_c + 1.0)
+    o0, l0 = oracle.attn(q, k, v_base, "bf16", scale=p.scale)
+    o1, l1 = oracle.attn(q, k, v_shift, "bf16", scale=p.scale)
+    assert np.abs(o1 - (o0 + 1.0)).max() < 1e-12 and np.abs(l1 - l0).max() < 1e-12
+
+
+def test_doubled_scale_equals_doubled_keys():
+    """Logits are scale * q . k: doubling the scale or doubling every key (exact in
+    bf16) gives the same output and LSE; the LSE also differs from the undoubled run."""
+    p, q, k, v = _small_problem(13)
+    k_f = _dec(torch.from_numpy(k.astype(np.int16)).view(torch.bfloat16))
+    k2 = _bf16(2.0 * k_f)
+    o_a, l_a = oracle.attn(q, k, v, "bf16", scale=2.0 * p.scale)
+    o_b, l_b = oracle.attn(q, k2, v, "bf16", scale=p.scale)
+    assert np.abs(o_a - o_b).max() < 1e-12 and np.abs(l_a - l_b).max() < 1e-12
+    _, l0 = oracle.attn(q, k, v, "bf16", scale=p.scale)
+    assert np.abs(l_a - l0).max() > 1e-3
+
+
+@pytest.mark.parametrize("S", [2, 7, 256])
+def test_merging_identical_states_adds_log2_of_their_count(S):
+    """S copies of one state (o, lse) merge to (o, lse + log2 S): equal weights 1/S."""
+    rng = np.random.default_rng(S)
+    o = rng.standard_normal((4, 8))
+    l = rng.uniform(-80, 80, 4)
+    mo, ml = oracle.merge(np.broadcast_to(o, (S, 4, 8)).copy(), np.broadcast_to(l, (S, 4)).copy())
+    assert np.abs(mo - o).max() < 1e-12
+    assert np.abs(ml - (l + math.log2(S))).max() < 1e-12
