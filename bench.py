@@ -28,7 +28,8 @@ the tiny LSE case) in us, GB/s or TFLOP/s and as a fraction of the roofline, plu
 the INT8 QK^T path (skv_sage_fwd, smoothing on) on the ring and dense problems, its
 fraction taken against the combined int8 + fp16 MFMA peak.  Secondary figures are
 the median (`us`) of 50 graph replays, each timed with its own HIP events, with
-p10 / p90 and the mean beside it.  `practical_ceilings` are the micro-benchmarks of
+p10 / p90 and the mean beside it; the prefill lines rotate four input copies between
+replays, so that no replay finds its inputs in the Infinity Cache.  `practical_ceilings` are the micro-benchmarks of
 microbench/ceilings.hip run in the same process (HBM read stream with plain and with
 nontemporal loads, bf16 MFMA, ...); every decode and prefill figure is also given
 as a fraction of them (`frac_practical`, `frac_mfma_practical`, and for prefill
@@ -179,25 +180,38 @@ def stats(xs):
 
 
 def time_graph(g, reps, warm=3):
-    """Per-replay GPU times (us) of a captured graph: HIP events around each of `reps`
-    replays, all queued behind a spin kernel that outlasts the host's enqueue time, so
-    host overhead opens no gaps.  Returns stats(): mean, p10, p50, p90."""
-    for _ in range(warm):
-        g.replay()
+    """Per-replay GPU times (us) of a captured graph, or of a list of graphs replayed in
+    rotation (replay i runs g[i % len(g)]): HIP events around each of `reps` replays,
+    all queued behind a spin kernel that outlasts the host's enqueue time, so host
+    overhead opens no gaps.  Returns stats(): mean, p10, p50, p90."""
+    gs = list(g) if isinstance(g, (list, tuple)) else [g]
+    for i in range(max(warm, len(gs))):
+        gs[i % len(gs)].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    g.replay()                      # host enqueue cost of one replay
+    gs[0].replay()                  # host enqueue cost of one replay
     host_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     torch.cuda._sleep(int(_spin_cycles_per_ms() * (3.0 * (host_ms + 0.05) * reps + 5.0)))
-    for a, b in evs:
+    for i, (a, b) in enumerate(evs):
         a.record()
-        g.replay()
+        gs[i % len(gs)].replay()
         b.record()
     torch.cuda.synchronize()
     return stats([a.elapsed_time(b) * 1e3 for a, b in evs])
+
+
+# Prefill lines replay NCOPY input copies in rotation, so that consecutive replays do not
+# find their inputs in the 256 MB Infinity Cache (NCOPY copies of each problem's inputs
+# exceed twice its size).
+NCOPY = 4
+
+
+def copies(*ts):
+    """NCOPY copies of each tensor: the tensor itself, then clones."""
+    return [[t] + [t.clone() for _ in range(NCOPY - 1)] for t in ts]
 
 
 def _spin_cycles_per_ms():
@@ -494,32 +508,33 @@ def secondary(skv, args, dec):
     # varlen causal prefill: 16 sequences, lengths U[128, 4096], Hq32 Hkv8 D128 bf16
     log("generating varlen_prefill")
     vl = wl.varlen_prefill(seed=4)
-    q, k, v = vl.q.cuda(), vl.k.cuda(), vl.v.cuda()
+    qs, ks, vs = copies(vl.q.cuda(), vl.k.cuda(), vl.v.cuda())
     cq, ck = vl.cu_seqlens_q.cuda(), vl.cu_seqlens_k.cuda()
-    out = torch.empty_like(q)
-    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(qs[0])
+    lse = torch.empty((qs[0].shape[1], qs[0].shape[0]), dtype=torch.float32, device="cuda")
     mx = max(vl.lengths)
 
-    def varlen():
-        skv.attn_fwd_varlen(q, k, v, cq, ck, mx, scale=vl.scale, causal=True, out=out, lse=lse)
+    def varlen(i):
+        return lambda: skv.attn_fwd_varlen(qs[i], ks[i], vs[i], cq, ck, mx, scale=vl.scale,
+                                           causal=True, out=out, lse=lse)
     phase("prefill varlen causal")
-    st = time_graph(capture(varlen), reps)
+    st = time_graph([capture(varlen(i)) for i in range(NCOPY)], reps)
     us = st["p50"]
     fl = wl.prefill_flops(vl.lengths, 32, 128, causal=True)
     tf = fl / (us * 1e-6) / 1e12
     res["prefill_varlen_causal_16seq_Hq32_Hkv8_D128"] = dict(
         **pct(st), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4),
         total_tokens=vl.meta["T"], flop=fl)
-    del q, k, v, out, lse
+    del qs, ks, vs, out, lse
     torch.cuda.empty_cache()
 
     # ring-style chunked prefill: B1 H16 S8192 D64 fp16, 4 KV chunks with smoothing + merge
     log("generating ring_chunks")
     rc = wl.ring_chunks(seed=5)
-    q = rc["q"].cuda()
-    kc = [t.cuda() for t in rc["k_chunks"]]
-    vc = [t.cuda() for t in rc["v_chunks"]]
-    kf, vf = rc["k"].cuda(), rc["v"].cuda()
+    qs, kfs, vfs = copies(rc["q"].cuda(), rc["k"].cuda(), rc["v"].cuda())
+    kcs = list(zip(*copies(*[t.cuda() for t in rc["k_chunks"]])))   # kcs[i][c]
+    vcs = list(zip(*copies(*[t.cuda() for t in rc["v_chunks"]])))
+    q = qs[0]
     po = torch.empty((4,) + tuple(q.shape), dtype=q.dtype, device="cuda")
     pl = torch.empty((4, 1, 16, 8192), dtype=torch.float32, device="cuda")
     mo = torch.empty_like(q)
@@ -527,18 +542,21 @@ def secondary(skv, args, dec):
     fo = torch.empty_like(q)
     fl_ = torch.empty((1, 16, 8192), dtype=torch.float32, device="cuda")
 
-    def ring():
-        for c in range(4):
-            skv.attn_fwd(q, kc[c], vc[c], scale=rc["scale"], smooth_k=True, out=po[c], lse=pl[c])
-        skv.merge_state(po, pl, out=mo, lse=ml)
+    def ring(i):
+        def f():
+            for c in range(4):
+                skv.attn_fwd(qs[i], kcs[i][c], vcs[i][c], scale=rc["scale"], smooth_k=True,
+                             out=po[c], lse=pl[c])
+            skv.merge_state(po, pl, out=mo, lse=ml)
+        return f
 
-    def full():
-        skv.attn_fwd(q, kf, vf, scale=rc["scale"], out=fo, lse=fl_)
+    def full(i):
+        return lambda: skv.attn_fwd(qs[i], kfs[i], vfs[i], scale=rc["scale"], out=fo, lse=fl_)
     fl = 4 * 16 * 8192 * 8192 * 64
     for name, fn in (("prefill_ring_4chunks_smooth_merge_H16_S8192_D64_fp16", ring),
                      ("prefill_full_H16_S8192_D64_fp16", full)):
         phase(name)
-        st = time_graph(capture(fn), reps)
+        st = time_graph([capture(fn(i)) for i in range(NCOPY)], reps)
         us = st["p50"]
         tf = fl / (us * 1e-6) / 1e12
         res[name] = dict(**pct(st), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4),
@@ -551,55 +569,59 @@ def secondary(skv, args, dec):
     wsf = torch.empty(skv.sage_workspace_bytes(1, 16, 16, 8192, 8192, 64, q.dtype, True),
                       dtype=torch.uint8, device="cuda")
 
-    def ring_int8():
-        for c in range(4):
-            skv.sage_fwd(q, kc[c], vc[c], scale=rc["scale"], smooth_k=True, out=po[c], lse=pl[c],
-                         workspace=wsr)
-        skv.merge_state(po, pl, out=mo, lse=ml)
+    def ring_int8(i):
+        def f():
+            for c in range(4):
+                skv.sage_fwd(qs[i], kcs[i][c], vcs[i][c], scale=rc["scale"], smooth_k=True,
+                             out=po[c], lse=pl[c], workspace=wsr)
+            skv.merge_state(po, pl, out=mo, lse=ml)
+        return f
 
-    def full_int8():
-        skv.sage_fwd(q, kf, vf, scale=rc["scale"], smooth_k=True, out=fo, lse=fl_, workspace=wsf)
+    def full_int8(i):
+        return lambda: skv.sage_fwd(qs[i], kfs[i], vfs[i], scale=rc["scale"], smooth_k=True,
+                                    out=fo, lse=fl_, workspace=wsf)
     for name, fn in (("prefill_int8qk_ring_4chunks_smooth_merge_H16_S8192_D64_fp16", ring_int8),
                      ("prefill_int8qk_full_smooth_H16_S8192_D64_fp16", full_int8)):
         phase(name)
-        st = time_graph(capture(fn), reps)
+        st = time_graph([capture(fn(i)) for i in range(NCOPY)], reps)
         us = st["p50"]
         tf = fl / (us * 1e-6) / 1e12
         res[name] = dict(**pct(st), tflops=round(tf, 1),
                          frac_mfma_int8_fp16=round(tf / INT8_FP16_PEAK_TFLOPS, 4), flop=fl)
-    del q, kc, vc, kf, vf, po, pl, mo, ml, fo, fl_, wsr, wsf
+    del q, qs, kcs, vcs, kfs, vfs, po, pl, mo, ml, fo, fl_, wsr, wsf
     torch.cuda.empty_cache()
 
     # dense non-causal D128 bf16 (the varlen problem's heads at one 8192-token
     # sequence): 16-bit path and INT8 QK^T path with smoothing
     log("generating dense D128 problem")
     p = wl.attn_problem(1, 32, 8, 8192, 8192, 128, seed=7)
-    q, k, v = p.q.cuda(), p.k.cuda(), p.v.cuda()
-    out = torch.empty_like(q)
+    qs, ks, vs = copies(p.q.cuda(), p.k.cuda(), p.v.cuda())
+    out = torch.empty_like(qs[0])
     lse = torch.empty((1, 32, 8192), dtype=torch.float32, device="cuda")
-    wsd = torch.empty(skv.sage_workspace_bytes(1, 32, 8, 8192, 8192, 128, q.dtype, True),
+    wsd = torch.empty(skv.sage_workspace_bytes(1, 32, 8, 8192, 8192, 128, qs[0].dtype, True),
                       dtype=torch.uint8, device="cuda")
 
-    def dense16():
-        skv.attn_fwd(q, k, v, scale=p.scale, out=out, lse=lse)
+    def dense16(i):
+        return lambda: skv.attn_fwd(qs[i], ks[i], vs[i], scale=p.scale, out=out, lse=lse)
 
-    def dense8():
-        skv.sage_fwd(q, k, v, scale=p.scale, smooth_k=True, out=out, lse=lse, workspace=wsd)
+    def dense8(i):
+        return lambda: skv.sage_fwd(qs[i], ks[i], vs[i], scale=p.scale, smooth_k=True, out=out,
+                                    lse=lse, workspace=wsd)
     fl = 4 * 32 * 8192 * 8192 * 128
     phase("prefill_dense_H32_Hkv8_S8192_D128_bf16")
-    st = time_graph(capture(dense16), reps)
+    st = time_graph([capture(dense16(i)) for i in range(NCOPY)], reps)
     us = st["p50"]
     tf = fl / (us * 1e-6) / 1e12
     res["prefill_dense_H32_Hkv8_S8192_D128_bf16"] = dict(
         **pct(st), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_PEAK_TFLOPS, 4), flop=fl)
     phase("prefill_int8qk_dense_smooth_H32_Hkv8_S8192_D128_bf16")
-    st = time_graph(capture(dense8), reps)
+    st = time_graph([capture(dense8(i)) for i in range(NCOPY)], reps)
     us = st["p50"]
     tf = fl / (us * 1e-6) / 1e12
     res["prefill_int8qk_dense_smooth_H32_Hkv8_S8192_D128_bf16"] = dict(
         **pct(st), tflops=round(tf, 1),
         frac_mfma_int8_fp16=round(tf / INT8_FP16_PEAK_TFLOPS, 4), flop=fl)
-    del q, k, v, out, lse, wsd
+    del qs, ks, vs, out, lse, wsd
     torch.cuda.empty_cache()
 
     # tiny LSE case: B1 H4 Sq64 Sk1000 D128 bf16 (launch-bound)
