@@ -14,9 +14,10 @@
 // PR).
 //
 // Per 32-key block and wave: S^T = K Q^T on v_mfma_f32_16x16x32 tiles (keys on M,
-// query rows on N), K fed straight from global memory in the operand layout
-// (k-step kk takes head-dim elements [32kk, 32kk + 32) of 16 key rows, the four
-// lanes of a row reading 64 contiguous bytes); O^T += V^T P^T with V staged in a
+// query rows on N), K fed straight from global memory in the operand layout at
+// D <= 128 (k-step kk takes head-dim elements [32kk, 32kk + 32) of 16 key rows, the
+// four lanes of a row reading 64 contiguous bytes) and, at D = 256, loaded in whole
+// rows and staged in a per-wave LDS slice like V; O^T += V^T P^T with V staged in a
 // per-wave LDS slice and read back with ds_read_b64_tr_b16, the key order of P
 // matching the C layout of S^T.
 #include "device.h"
