@@ -1,8 +1,8 @@
 // ceilings.hip -- micro-benchmarks for the practical ceilings the attention kernels
 // are measured against on MI355X (gfx950): LDS read bandwidth (16-byte reads and
 // the 64-bit transpose read), bf16 MFMA throughput, v_exp_f32 and v_fma_f32 issue
-// rates, alone and interleaved (whether exponentials and FMAs share one pipe), and an
-// HBM read stream (plain and nontemporal loads).  Measurement infrastructure only; nothing
+// rates, alone and interleaved (whether exponentials and FMAs share one pipe), the MFMA
+// rate and shader clock sustained over a long run, and an HBM read stream (plain and nontemporal loads).  Measurement infrastructure only; nothing
 // in the attention library uses it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -61,6 +61,34 @@ __global__ __launch_bounds__(256) void mfma_bf16(float* out, int iters) {
   f32x16 s = c0 + c1 + c2 + c3;
   float r = 0; for (int j = 0; j < 16; ++j) r += s[j];
   if (r == 1234.5f) out[blockIdx.x] = r;
+}
+// The same MFMA stream, long enough (tens to hundreds of ms) for the chip's power
+// management to settle, with the shader clock it ran at: work group 0's first lane
+// records s_memtime (shader clock) and s_memrealtime (100 MHz) at its start and end.
+__global__ __launch_bounds__(256) void mfma_bf16_clocked(unsigned long long* out, int iters) {
+  unsigned long long t0 = 0, r0 = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  bf16x8 a, b;
+  for (int j = 0; j < 8; ++j) { a[j] = (__bf16)(threadIdx.x * 0.001f + j); b[j] = (__bf16)(j * 0.5f); }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  f32x16 s = c0 + c1 + c2 + c3;
+  float r = 0; for (int j = 0; j < 16; ++j) r += s[j];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    out[0] = t1 - t0;
+    out[1] = r1 - r0;
+    out[2] = r == 1234.5f ? 1ull : 0ull;   // keeps the accumulators live
+  }
 }
 // exp2 throughput
 __global__ __launch_bounds__(256) void exp_f32(float* out, int iters) {
@@ -146,6 +174,7 @@ extern "C" int run(int which, void* p, int64_t n, void* out, int grid, int iters
     case 7: hipLaunchKernelGGL(exp_only, dim3(grid), dim3(256), 0, s, (float*)out, iters); break;
     case 8: hipLaunchKernelGGL(exp_fma<1>, dim3(grid), dim3(256), 0, s, (float*)out, iters); break;
     case 9: hipLaunchKernelGGL(exp_fma<3>, dim3(grid), dim3(256), 0, s, (float*)out, iters); break;
+    case 10: hipLaunchKernelGGL(mfma_bf16_clocked, dim3(grid), dim3(256), 0, s, (unsigned long long*)out, iters); break;
   }
   return (int)hipGetLastError();
 }

@@ -67,6 +67,14 @@ def measure():
     res["fma_over_exp_time_2waves"] = t_fma / t_exp
     res["exp_plus_fma_over_exp_time_2waves"] = t(8, g3, 4000) / t_exp
     res["exp_plus_3fma_over_exp_time_2waves"] = t(9, g3, 4000) / t_exp
+    # The same MFMA stream for about a quarter of a second per launch, when the chip's power
+    # management has settled: the rate and the shader clock it holds (s_memtime ticks
+    # per s_memrealtime tick at 100 MHz, from work group 0)
+    g4, it4 = CU * 2, 2_000_000
+    sec = t(10, g4, it4, reps=2)
+    clk = out[:6].cpu().view(torch.int64)
+    res["mfma_bf16_32x32x16_sustained_tflops"] = g4 * 4 * 4 * 32768 * it4 / sec / 1e12
+    res["mfma_sustained_shader_clock_ghz"] = float(clk[0]) / float(clk[1]) * 0.1
     buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
     for which, key in ((5, "hbm_read_stream_GBs"), (6, "hbm_read_stream_nontemporal_GBs")):
         best = 0.0
